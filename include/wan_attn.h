@@ -1,0 +1,116 @@
+/*
+ * wan_attn.h -- C ABI of the MI355X (gfx950) attention forward for Wan video DiT blocks.
+ *
+ * Operation (every entry point below computes it, or a stage of it):
+ *   O[b, i, h, :] = sum_j softmax_j( Q[b,i,h,:] . K[b,j,h,:] / sqrt(head_dim) ) * V[b, j, h, :]
+ * non-causal and unmasked: the full spatio-temporal self-attention over the video tokens of a Wan
+ * DiT block, and its cross-attention to the 512 umT5 text tokens ("Wan 2.1: VBench 86.22% ..."
+ * explainer of the Wan technical report, sections "先看现象" -- non-causal attention, forward cost
+ * beta = 4 in C = L(alpha*b*s*h^2 + beta*b*s^2*h) -- and "干预与形式化", DiT backbone paragraph).
+ * The scale is fixed at 1/sqrt(head_dim); there is no mask argument.
+ *
+ * Layouts (all entry points): row-major, dense, contiguous, device memory
+ *   q, o : [batch, s_q,  heads, head_dim]  bfloat16
+ *   k, v : [batch, s_kv, heads, head_dim]  bfloat16
+ * head_dim must be 128.  Pointers must be 16-byte aligned.  o must not overlap q, k or v.
+ *
+ * Ownership: the caller owns every buffer it passes; the library never frees or retains them.
+ * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is the default stream)
+ * and returns; results are ready when the stream reaches that point.  A fault inside a kernel
+ * surfaces at the caller's next synchronisation, not in the return code.
+ * Errors: every function returns WAN_ATTN_OK (0) or a negative code below; it never aborts and
+ * never prints unless the environment variable WAN_ATTN_LOG=1 is set.  Argument checks happen
+ * before any work is enqueued, so a failed check leaves the stream untouched.
+ */
+#ifndef WAN_ATTN_H
+#define WAN_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WAN_ATTN_VERSION 1
+
+/* Arithmetic of the call (the `dtype` argument). */
+enum wan_attn_dtype {
+  /* bf16 x bf16 MFMA products with fp32 accumulation, fp32 online softmax, bf16 output. */
+  WAN_ATTN_BF16 = 0,
+  /* The 8-bit scheme of the Wan inference optimisations ("Wan 2.1: VBench 86.22% ..." explainer,
+   * section "干预与形式化"; "Wan模型是什么它能做什么" explainer, section 4.2): Q and K in int8 for
+   * QK^T, P and V in FP8 (OCP e4m3) for PV, fp32 accumulation across KV blocks.  The library
+   * quantises the bf16 inputs itself (see wan_attn8_quantize) into stream-ordered scratch memory
+   * it allocates and frees on `stream`.  Output is bf16. */
+  WAN_ATTN_INT8_FP8 = 1
+};
+
+/* Return codes. */
+enum wan_attn_status {
+  WAN_ATTN_OK = 0,
+  WAN_ATTN_EINVAL = -1,        /* null pointer, non-positive size, unknown dtype, overflow   */
+  WAN_ATTN_EALIGN = -2,        /* a pointer is not 16-byte aligned                            */
+  WAN_ATTN_ENOMEM = -3,        /* scratch allocation failed                                   */
+  WAN_ATTN_ELAUNCH = -4,       /* the HIP runtime refused a launch or a query                 */
+  WAN_ATTN_EUNSUPPORTED = -5   /* head_dim other than 128                                     */
+};
+
+/*
+ * Attention forward.  q, k, v, o as in the header comment; batch, heads, s_q, s_kv >= 1;
+ * head_dim == 128; dtype is a wan_attn_dtype; stream is a hipStream_t or NULL.
+ * bf16: needs no scratch memory.  int8_fp8: allocates about s_q*heads*batch*(head_dim+4) +
+ * s_kv*heads*batch*(2*head_dim+4) bytes of scratch on `stream`, freed on `stream` after use.
+ */
+int wan_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                 int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                 int64_t head_dim, int dtype, void* stream);
+
+/*
+ * First stage of the 8-bit path, exposed so that its integer outputs can be checked code for
+ * code and the second stage timed alone.  Inputs q, k, v as above (bf16).  Outputs, all device
+ * memory owned by the caller:
+ *   q_codes [batch, s_q, heads, 128] int8     k_codes [batch, s_kv, heads, 128] int8
+ *   q_scale [batch, heads, ceil(s_q/64)]  f32 k_scale [batch, heads, ceil(s_kv/64)] f32
+ *   v_codes [batch, heads, 128, s_kv_pad] e4m3 bytes, V transposed per head, s_kv_pad =
+ *           ceil(s_kv/64)*64, zero bytes in the padding
+ *   v_scale [batch, heads, 128] f32           smooth  [batch, heads, 128] f32
+ * Per (batch, head): smooth[c] = sqrt(max_t|K[t,c]| / max_t|Q[t,c]|) (1 if either is 0);
+ * Q' = Q*smooth, K' = K*(1/smooth) in fp32; one int8 scale per 64-token block of Q' (K') over all
+ * channels: inv = 127/amax, code = clamp(rne(x*inv), -127, 127), scale = amax/127 (amax = 0:
+ * codes 0, scale 1); V: one scale per channel over all tokens: inv = 448/amax,
+ * code = e4m3(clamp(V*inv, +-448)) with round-to-nearest-even, scale = amax/448.
+ * scratch must hold wan_attn8_quantize_scratch_bytes(batch, heads) bytes (16-byte aligned).
+ */
+int wan_attn8_quantize(const void* q, const void* k, const void* v,
+                       int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim,
+                       void* q_codes, void* q_scale, void* k_codes, void* k_scale,
+                       void* v_codes, void* v_scale, void* smooth, void* scratch, void* stream);
+
+/* Bytes of scratch wan_attn8_quantize needs (per-channel maxima of Q, K and V). */
+size_t wan_attn8_quantize_scratch_bytes(int64_t batch, int64_t heads);
+
+/*
+ * Second stage of the 8-bit path: attention from the quantised operands of wan_attn8_quantize
+ * (same layouts and meaning), writing o [batch, s_q, heads, 128] bf16:
+ *   S = int32(q_code . k_code) * q_scale * k_scale / sqrt(128);  online softmax in fp32 over
+ *   64-key blocks;  P~ = e4m3(p * 256);  O = alpha*O + P~ . V~ (fp8 MFMA, fp32 accumulation);
+ *   l = alpha*l + sum p;  out = bf16(O * v_scale[c] / (256 * l)).
+ */
+int wan_attn8_fwd_quantized(const void* q_codes, const void* q_scale,
+                            const void* k_codes, const void* k_scale,
+                            const void* v_codes, const void* v_scale, void* o,
+                            int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                            int64_t head_dim, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* wan_attn_strerror(int code);
+
+/* WAN_ATTN_VERSION of the built library. */
+int wan_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WAN_ATTN_H */

@@ -1,0 +1,162 @@
+"""Pins of the 8-bit scheme emulator (oracle.attn8) against things other than itself.
+
+* Quantisation against its defining bounds: every int8 code is within half a step of x * inv, the
+  block maximum maps to +-127, every e4m3 value is within the format's relative half-step of
+  V * inv, the channel maximum maps to +-448; exactly representable inputs round-trip exactly.
+* Smoothing balances the per-channel maxima of Q' and K' and leaves QK^T unchanged (fp64 check).
+* Special cases that reduce to the exact attention: one key returns its V row; with exactly
+  representable operands the only error left is the FP8 rounding of P, bounded by 2^-4 * max|V|.
+* The judged 8-bit bounds of the task (rel-L2 <= 6e-2, cosine >= 0.995 against exact attention) on
+  a small seeded workload with 1% outlier channels at 8 sigma, and that the literal scheme without
+  smoothing is worse there.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attn8
+
+
+def _bf16(x):
+    return oracle.bf16_round(np.asarray(x, np.float32))
+
+
+def _gauss(shape, seed, sigma=1.0):
+    return _bf16(np.random.default_rng(seed).standard_normal(shape) * sigma)
+
+
+def _metrics(got, ref):
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    cos = got @ ref / (np.linalg.norm(got) * np.linalg.norm(ref))
+    return rel, cos
+
+
+def test_int8_block_quantisation_bounds():
+    x = _gauss((200, 128), 1, 3.0)
+    codes, scales = attn8._block_int8(x, 64)
+    assert codes.shape == x.shape and scales.shape == (4,)
+    for blk in range(4):
+        xb = x[blk * 64:(blk + 1) * 64].astype(np.float64)
+        cb = codes[blk * 64:(blk + 1) * 64].astype(np.float64)
+        amax = np.abs(xb).max()
+        assert np.isclose(scales[blk], amax / 127, rtol=2 ** -23)
+        assert np.max(np.abs(cb)) == 127
+        assert np.max(np.abs(cb - xb * (127 / amax))) <= 0.5 + 1e-4
+    z, zs = attn8._block_int8(np.zeros((70, 128), np.float32), 64)
+    assert not z.any() and np.all(zs == 1)
+
+
+def test_int8_exact_roundtrip():
+    x = np.random.default_rng(2).integers(-127, 128, size=(64, 128)).astype(np.float32)
+    x[3, 7] = 127.0
+    codes, scales = attn8._block_int8(x, 64)
+    np.testing.assert_array_equal(codes, x.astype(np.int8))
+    assert scales[0] == 1.0
+
+
+def test_e4m3_channel_quantisation_bounds():
+    v = _gauss((300, 128), 3, 2.0)
+    codes, scale = attn8._channel_e4m3(v)
+    vals = oracle.e4m3fn_decode(codes)
+    amax = np.abs(v).max(axis=0).astype(np.float64)
+    np.testing.assert_allclose(scale, amax / 448, rtol=2 ** -23)
+    assert np.all(np.abs(vals).max(axis=0) == 448)
+    t = v.astype(np.float64) * (448 / amax)
+    normal = np.abs(t) >= 2 ** -6
+    assert np.all(np.abs(vals - t)[normal] <= np.abs(t)[normal] * 2 ** -4 * (1 + 1e-6))
+    assert np.all(np.abs(vals - t)[~normal] <= 2 ** -10 * (1 + 1e-6))
+
+
+def test_smoothing_balances_and_preserves_products():
+    rng = np.random.default_rng(4)
+    q = _bf16(rng.standard_normal((100, 128)) * rng.uniform(0.1, 10, 128))
+    k = _bf16(rng.standard_normal((90, 128)) * rng.uniform(0.1, 10, 128))
+    z = attn8.quantize_head(q, k, k, smooth=True)
+    a = z["alpha"].astype(np.float64)
+    qs, ks = q * a, k / a
+    np.testing.assert_allclose(np.abs(qs).max(0), np.abs(ks).max(0), rtol=1e-6)
+    np.testing.assert_allclose(qs @ ks.T, q.astype(np.float64) @ k.astype(np.float64).T,
+                               rtol=1e-6, atol=1e-9)
+
+
+def test_single_key_returns_value_row():
+    q = _gauss((1, 10, 2, 128), 5)
+    k = _gauss((1, 1, 2, 128), 6)
+    # V values are e4m3 values and each channel's maximum is 448, so V quantises exactly
+    v = oracle.e4m3fn_round(np.random.default_rng(7).standard_normal((1, 1, 2, 128)) * 100)
+    v[..., :] = np.where(np.abs(v) > 0, np.sign(v) * 448.0, 448.0)
+    rows = np.array([[0, h, i] for h in range(2) for i in range(10)])
+    got = oracle.attn8_emulate(q, k, v.astype(np.float32), rows)
+    np.testing.assert_array_equal(got, v[0, 0][rows[:, 1]].astype(np.float32))
+
+
+def test_exact_operands_leave_only_fp8_rounding_of_p():
+    rng = np.random.default_rng(8)
+    s, d = 256, 128
+    # int8-exact Q, K: integers with a 127 in every 64-row block; no smoothing
+    q = rng.integers(-127, 128, (1, 64, 1, d)).astype(np.float32) / 64
+    k = rng.integers(-127, 128, (1, s, 1, d)).astype(np.float32) / 64
+    q[0, 0, 0, 0] = 127 / 64
+    k[0, ::64, 0, 0] = 127 / 64
+    vv = oracle.e4m3fn_round(rng.standard_normal((1, s, 1, d)) * 50)
+    vv[0, 0, 0, :] = 448.0
+    v = vv.astype(np.float32)
+    rows = np.array([[0, 0, i] for i in range(64)])
+    got = oracle.attn8_emulate(q, k, v, rows, smooth=False).astype(np.float64)
+    ref = oracle.attention_rows(q, k, v, rows)
+    bound = 2 ** -4 * np.abs(v).max() + 2 ** -8 * np.abs(ref)
+    assert np.all(np.abs(got - ref) <= bound)
+    # and the bound is not trivially loose: the mean error is far below it
+    assert np.mean(np.abs(got - ref)) < 0.1 * 2 ** -4 * np.abs(v).max()
+
+
+def _outlier_case(seed, H=4, s=8192, d=128, n_rows=48):
+    rng = np.random.default_rng(seed)
+    def draw():
+        x = rng.standard_normal((1, s, H, d))
+        cols = rng.choice(H * d, size=max(1, round(0.01 * H * d)), replace=False)
+        x.reshape(1, s, H * d)[:, :, cols] *= 8
+        return _bf16(x)
+    q, k, v = draw(), draw(), draw()
+    rows = np.array([[0, h, i] for h in range(H) for i in rng.choice(s, n_rows, replace=False)])
+    return q, k, v, rows
+
+
+def test_judged_bounds_with_outliers_and_literal_scheme_is_worse():
+    q, k, v, rows = _outlier_case(9)
+    ref = oracle.attention_rows(q, k, v, rows)
+    rel_s, cos_s = _metrics(oracle.attn8_emulate(q, k, v, rows, smooth=True), ref)
+    rel_l, cos_l = _metrics(oracle.attn8_emulate(q, k, v, rows, smooth=False), ref)
+    assert rel_s <= 6e-2 and cos_s >= 0.995
+    assert rel_l > rel_s
+
+
+def test_kv_block_size_changes_only_rounding():
+    q, k, v, rows = _outlier_case(10, H=2, s=2048, n_rows=32)
+    a = oracle.attn8_emulate(q, k, v, rows, kv_block=64)
+    b = oracle.attn8_emulate(q, k, v, rows, kv_block=128)
+    rel, _ = _metrics(a, b)
+    assert rel < 2e-2
+
+
+@pytest.mark.parametrize("where", ["p_scale", "v_scale"])
+def test_planted_mistakes_are_caught(monkeypatch, where):
+    """A dropped factor in the emulator breaks the exact-operand pin above."""
+    rng = np.random.default_rng(11)
+    q = _gauss((1, 64, 1, 128), 12)
+    k = _gauss((1, 128, 1, 128), 13)
+    v = _gauss((1, 128, 1, 128), 14)
+    rows = np.array([[0, 0, i] for i in range(64)])
+    ref = oracle.attention_rows(q, k, v, rows)
+    if where == "p_scale":
+        monkeypatch.setattr(attn8, "e4m3fn_round", lambda x: oracle.e4m3fn_round(np.asarray(x) / 256.0))
+    else:
+        orig = attn8._channel_e4m3
+        monkeypatch.setattr(attn8, "_channel_e4m3", lambda vh: (orig(vh)[0], np.ones(vh.shape[1], np.float32)))
+    bad = oracle.attn8_emulate(q, k, v, rows)
+    rel, _ = _metrics(bad, ref)
+    assert rel > 0.2
+    del rng
