@@ -1,0 +1,92 @@
+"""The C ABI library on the host, without a GPU: it loads, exports every function that
+include/wan_attn.h declares, and rejects bad arguments before any GPU work (the checks return
+before the first HIP call, so these run on a machine without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import video_diffusion_transformer_wan_amd as wan
+from _util import ensure_built
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "wan_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wan_attn\w*)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ensure_built()
+    names = declared_functions()
+    assert "wan_attn_fwd" in names and len(names) >= 6
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strerror():
+    ensure_built()
+    assert wan.wan_attn_version() == 1
+    for code in (0, -1, -2, -3, -4, -5):
+        assert len(wan.wan_attn_strerror(code)) > 5
+    assert wan.wan_attn_strerror(123) == "unknown status code"
+
+
+def _fwd(q=16, k=32, v=48, o=4096, b=1, H=1, sq=1, skv=1, d=128, dtype=0):
+    lib = ensure_built()
+    return lib.wan_attn_fwd(q, k, v, o, b, H, sq, skv, d, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), wan.WAN_ATTN_EINVAL),
+    (dict(o=None), wan.WAN_ATTN_EINVAL),
+    (dict(b=0), wan.WAN_ATTN_EINVAL),
+    (dict(H=-1), wan.WAN_ATTN_EINVAL),
+    (dict(sq=0), wan.WAN_ATTN_EINVAL),
+    (dict(skv=0), wan.WAN_ATTN_EINVAL),
+    (dict(d=64), wan.WAN_ATTN_EUNSUPPORTED),
+    (dict(d=0), wan.WAN_ATTN_EINVAL),
+    (dict(dtype=2), wan.WAN_ATTN_EINVAL),
+    (dict(dtype=-1), wan.WAN_ATTN_EINVAL),
+    (dict(q=17), wan.WAN_ATTN_EALIGN),
+    (dict(v=40), wan.WAN_ATTN_EALIGN),
+    (dict(o=16), wan.WAN_ATTN_EINVAL),            # output overlaps q
+    (dict(sq=1 << 31), wan.WAN_ATTN_EINVAL),      # token count beyond the kernels' counters
+])
+def test_argument_checks(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_quantize_argument_checks():
+    lib = ensure_built()
+    ptrs = [16 * (i + 1) for i in range(11)]
+    args = ptrs[:3] + [1, 1, 64, 64, 128] + ptrs[3:] + [None]
+    bad = list(args)
+    bad[7] = 96
+    assert lib.wan_attn8_quantize(*bad) == wan.WAN_ATTN_EUNSUPPORTED
+    bad = list(args)
+    bad[8] = None
+    assert lib.wan_attn8_quantize(*bad) == wan.WAN_ATTN_EINVAL
+    bad = list(args)
+    bad[9] = 20
+    assert lib.wan_attn8_quantize(*bad) == wan.WAN_ATTN_EALIGN
+    assert lib.wan_attn8_quantize_scratch_bytes(2, 3) == 2 * 3 * 3 * 128 * 4
+    assert lib.wan_attn8_quantize_scratch_bytes(0, 3) == 0
+    fargs = [16 * (i + 1) for i in range(7)] + [1, 1, 64, 64, 128, None]
+    bad = list(fargs)
+    bad[6] = None
+    assert lib.wan_attn8_fwd_quantized(*bad) == wan.WAN_ATTN_EINVAL
+    bad = list(fargs)
+    bad[10] = 0
+    assert lib.wan_attn8_fwd_quantized(*bad) == wan.WAN_ATTN_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(wan, "_lib", None)
+    monkeypatch.setattr(wan, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        wan.lib()

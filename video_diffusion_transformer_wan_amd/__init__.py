@@ -1,0 +1,182 @@
+"""Python binding of the Wan attention library (libwan_attn.so, hand-written HIP for gfx950).
+
+Argument marshalling only: every step of the attention runs in the library's kernels.  The
+functions below carry the C ABI's names (include/wan_attn.h) and take either raw device
+addresses (ints) or torch tensors for the pointer arguments; torch serves for device memory and
+streams.  ``attention`` is a convenience wrapper that allocates the output.
+
+The library must have been built (``video_diffusion_transformer_wan_amd.build.build()``); there is
+no fallback -- loading fails loudly when it is missing.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwan_attn.so")
+
+WAN_ATTN_BF16 = 0
+WAN_ATTN_INT8_FP8 = 1
+DTYPES = {"bf16": WAN_ATTN_BF16, "int8_fp8": WAN_ATTN_INT8_FP8}
+
+WAN_ATTN_OK = 0
+WAN_ATTN_EINVAL = -1
+WAN_ATTN_EALIGN = -2
+WAN_ATTN_ENOMEM = -3
+WAN_ATTN_ELAUNCH = -4
+WAN_ATTN_EUNSUPPORTED = -5
+
+QUANT_BLOCK = 64
+HEAD_DIM = 128
+
+
+class WanAttnError(RuntimeError):
+    def __init__(self, code, fn):
+        self.code = code
+        super().__init__(f"{fn} failed with {code}: {wan_attn_strerror(code)}")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+_SIGNATURES = {
+    "wan_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, ctypes.c_int, _P]),
+    "wan_attn8_quantize": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I64, _I64,
+                                          _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "wan_attn8_quantize_scratch_bytes": (ctypes.c_size_t, [_I64, _I64]),
+    "wan_attn8_fwd_quantized": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P,
+                                               _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "wan_attn_version": (ctypes.c_int, []),
+}
+
+
+def lib():
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "video_diffusion_transformer_wan_amd.build.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc, fn):
+    if rc != WAN_ATTN_OK:
+        raise WanAttnError(rc, fn)
+
+
+def wan_attn_strerror(code):
+    return lib().wan_attn_strerror(code).decode()
+
+
+def wan_attn_version():
+    return lib().wan_attn_version()
+
+
+def wan_attn_fwd(q, k, v, o, batch, heads, s_q, s_kv, head_dim, dtype, stream=None):
+    dtype = DTYPES.get(dtype, dtype)
+    rc = lib().wan_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, s_q, s_kv, head_dim,
+                            dtype, _stream(stream))
+    _check(rc, "wan_attn_fwd")
+
+
+def wan_attn8_quantize_scratch_bytes(batch, heads):
+    return lib().wan_attn8_quantize_scratch_bytes(batch, heads)
+
+
+def wan_attn8_quantize(q, k, v, batch, heads, s_q, s_kv, head_dim, q_codes, q_scale, k_codes,
+                       k_scale, v_codes, v_scale, smooth, scratch, stream=None):
+    rc = lib().wan_attn8_quantize(_ptr(q), _ptr(k), _ptr(v), batch, heads, s_q, s_kv, head_dim,
+                                  _ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale),
+                                  _ptr(v_codes), _ptr(v_scale), _ptr(smooth), _ptr(scratch),
+                                  _stream(stream))
+    _check(rc, "wan_attn8_quantize")
+
+
+def wan_attn8_fwd_quantized(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o, batch, heads,
+                            s_q, s_kv, head_dim, stream=None):
+    rc = lib().wan_attn8_fwd_quantized(_ptr(q_codes), _ptr(q_scale), _ptr(k_codes), _ptr(k_scale),
+                                       _ptr(v_codes), _ptr(v_scale), _ptr(o), batch, heads, s_q,
+                                       s_kv, head_dim, _stream(stream))
+    _check(rc, "wan_attn8_fwd_quantized")
+
+
+def _check_tensors(q, k, v):
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-d bfloat16 CUDA tensor [b, s, H, d]")
+    b, s_q, H, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[2] != H or k.shape[3] != d:
+        raise ValueError("k and v must be [b, s_kv, H, d] matching q [b, s_q, H, d]")
+    return b, H, s_q, k.shape[1], d
+
+
+def attention(q, k, v, dtype="bf16", out=None, stream=None):
+    """softmax(q k^T / sqrt(d)) v per (batch, head) for q [b, s_q, H, 128], k, v [b, s_kv, H, 128]
+    bfloat16 CUDA tensors; returns a new (or fills ``out``) [b, s_q, H, 128] bfloat16 tensor."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    wan_attn_fwd(q, k, v, out, b, H, s_q, s_kv, d, dtype, stream)
+    return out
+
+
+def attention8_quantize(q, k, v, stream=None):
+    """Stage 1 of the 8-bit path on torch tensors; returns a dict of the codes and scales
+    (layouts as in include/wan_attn.h)."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    nbq = -(-s_q // QUANT_BLOCK)
+    nbk = -(-s_kv // QUANT_BLOCK)
+    dev = q.device
+    out = dict(
+        q_codes=torch.empty((b, s_q, H, d), dtype=torch.int8, device=dev),
+        k_codes=torch.empty((b, s_kv, H, d), dtype=torch.int8, device=dev),
+        q_scale=torch.empty((b, H, nbq), dtype=torch.float32, device=dev),
+        k_scale=torch.empty((b, H, nbk), dtype=torch.float32, device=dev),
+        v_codes=torch.empty((b, H, d, nbk * QUANT_BLOCK), dtype=torch.uint8, device=dev),
+        v_scale=torch.empty((b, H, d), dtype=torch.float32, device=dev),
+        smooth=torch.empty((b, H, d), dtype=torch.float32, device=dev),
+    )
+    scratch = torch.empty(wan_attn8_quantize_scratch_bytes(b, H) // 4, dtype=torch.float32, device=dev)
+    wan_attn8_quantize(q, k, v, b, H, s_q, s_kv, d, out["q_codes"], out["q_scale"], out["k_codes"],
+                       out["k_scale"], out["v_codes"], out["v_scale"], out["smooth"], scratch, stream)
+    out["_scratch"] = scratch
+    return out
+
+
+def attention8_from_quantized(z, b, H, s_q, s_kv, out=None, stream=None):
+    """Stage 2 of the 8-bit path from the dict of ``attention8_quantize``."""
+    import torch
+    if out is None:
+        out = torch.empty((b, s_q, H, HEAD_DIM), dtype=torch.bfloat16, device=z["q_codes"].device)
+    wan_attn8_fwd_quantized(z["q_codes"], z["q_scale"], z["k_codes"], z["k_scale"], z["v_codes"],
+                            z["v_scale"], out, b, H, s_q, s_kv, HEAD_DIM, stream)
+    return out

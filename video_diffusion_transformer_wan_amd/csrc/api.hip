@@ -1,0 +1,232 @@
+// C ABI of the Wan attention library: argument checks, dispatch, scratch memory.
+// The contract of every entry point is documented in include/wan_attn.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <mutex>
+
+#include "wan_attn.h"
+#include "wan_attn_internal.h"
+
+namespace {
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("WAN_ATTN_LOG");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+#define WAN_LOG(...)                          \
+  do {                                        \
+    if (log_enabled()) {                      \
+      std::fprintf(stderr, "[wan_attn] " __VA_ARGS__); \
+      std::fputc('\n', stderr);               \
+    }                                         \
+  } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Shape checks shared by every entry point.  Sizes must be positive, the head dimension 128, and
+// every index the kernels form must fit their 32-bit counters (tokens, tiles) and 64-bit offsets.
+int check_shape(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim) {
+  if (batch < 1 || heads < 1 || s_q < 1 || s_kv < 1 || head_dim < 1) return WAN_ATTN_EINVAL;
+  if (head_dim != wan::kHeadDim) return WAN_ATTN_EUNSUPPORTED;
+  const int64_t kMax32 = 0x7fffffffLL;
+  if (batch > kMax32 || heads > kMax32 || s_q > kMax32 - 256 || s_kv > kMax32 - 256)
+    return WAN_ATTN_EINVAL;
+  // workgroup count (256-row query tiles) must fit in int; element counts in 2^60
+  const long double tiles = (long double)wan::ceil_div(s_q, 64) * (long double)batch * heads;
+  if (tiles > (long double)kMax32 - 8) return WAN_ATTN_EINVAL;
+  const long double elems = (long double)batch * heads * (long double)(s_q > s_kv ? s_q : s_kv) * head_dim;
+  if (elems > (long double)(1LL << 60)) return WAN_ATTN_EINVAL;
+  return WAN_ATTN_OK;
+}
+
+int check_qkvo(const void* q, const void* k, const void* v, const void* o, int64_t batch,
+               int64_t heads, int64_t s_q, int64_t s_kv) {
+  if (!q || !k || !v || !o) return WAN_ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return WAN_ATTN_EALIGN;
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
+  const int64_t kb = batch * s_kv * heads * wan::kHeadDim * 2;
+  if (overlaps(o, qb, q, qb) || overlaps(o, qb, k, kb) || overlaps(o, qb, v, kb)) return WAN_ATTN_EINVAL;
+  return WAN_ATTN_OK;
+}
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return WAN_ATTN_OK;
+  WAN_LOG("%s failed: %s", what, hipGetErrorString(e));
+  return e == hipErrorOutOfMemory ? WAN_ATTN_ENOMEM : WAN_ATTN_ELAUNCH;
+}
+
+// Per-device stream-ordered pool for the 8-bit path's scratch; memory freed on a stream returns
+// to the pool and is reused by later calls instead of going back to the driver.
+std::mutex g_pool_mu;
+hipMemPool_t g_pools[64] = {};
+
+int pool_for_current_device(hipMemPool_t* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return WAN_ATTN_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  if (!g_pools[dev]) {
+    hipMemPoolProps props = {};
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    hipMemPool_t pool;
+    if (hipMemPoolCreate(&pool, &props) != hipSuccess) return WAN_ATTN_ELAUNCH;
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    g_pools[dev] = pool;
+  }
+  *out = g_pools[dev];
+  return WAN_ATTN_OK;
+}
+
+struct Attn8Layout {
+  size_t q_codes, k_codes, q_scale, k_scale, v_codes, v_scale, smooth, chan_max, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+Attn8Layout attn8_layout(int64_t b, int64_t H, int64_t s_q, int64_t s_kv) {
+  Attn8Layout L;
+  const size_t nbq = (size_t)wan::ceil_div(s_q, wan::kQuantBlock);
+  const size_t nbk = (size_t)wan::ceil_div(s_kv, wan::kQuantBlock);
+  const size_t skv_pad = nbk * wan::kQuantBlock;
+  size_t off = 0;
+  L.q_codes = off; off = align256(off + (size_t)b * s_q * H * wan::kHeadDim);
+  L.k_codes = off; off = align256(off + (size_t)b * s_kv * H * wan::kHeadDim);
+  L.v_codes = off; off = align256(off + (size_t)b * H * wan::kHeadDim * skv_pad);
+  L.q_scale = off; off = align256(off + (size_t)b * H * nbq * 4);
+  L.k_scale = off; off = align256(off + (size_t)b * H * nbk * 4);
+  L.v_scale = off; off = align256(off + (size_t)b * H * wan::kHeadDim * 4);
+  L.smooth = off;  off = align256(off + (size_t)b * H * wan::kHeadDim * 4);
+  L.chan_max = off; off = align256(off + (size_t)b * H * 3 * wan::kHeadDim * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wan_attn_version(void) { return WAN_ATTN_VERSION; }
+
+const char* wan_attn_strerror(int code) {
+  switch (code) {
+    case WAN_ATTN_OK: return "success";
+    case WAN_ATTN_EINVAL: return "invalid argument (null pointer, bad size, unknown dtype or overlapping output)";
+    case WAN_ATTN_EALIGN: return "pointer not 16-byte aligned";
+    case WAN_ATTN_ENOMEM: return "out of device memory for scratch";
+    case WAN_ATTN_ELAUNCH: return "HIP runtime error while launching";
+    case WAN_ATTN_EUNSUPPORTED: return "unsupported head_dim (only 128)";
+    default: return "unknown status code";
+  }
+}
+
+size_t wan_attn8_quantize_scratch_bytes(int64_t batch, int64_t heads) {
+  if (batch < 1 || heads < 1) return 0;
+  return (size_t)batch * heads * 3 * wan::kHeadDim * sizeof(float);
+}
+
+int wan_attn8_quantize(const void* q, const void* k, const void* v, int64_t batch, int64_t heads,
+                       int64_t s_q, int64_t s_kv, int64_t head_dim, void* q_codes, void* q_scale,
+                       void* k_codes, void* k_scale, void* v_codes, void* v_scale, void* smooth,
+                       void* scratch, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  if (!q || !k || !v || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale ||
+      !smooth || !scratch)
+    return WAN_ATTN_EINVAL;
+  const void* ptrs[] = {q, k, v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, smooth, scratch};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  WAN_LOG("quantize b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads,
+          (long long)s_q, (long long)s_kv);
+  return from_hip(wan::launch_attn8_quantize(
+                      q, k, v, sh, static_cast<int8_t*>(q_codes), static_cast<float*>(q_scale),
+                      static_cast<int8_t*>(k_codes), static_cast<float*>(k_scale),
+                      static_cast<uint8_t*>(v_codes), static_cast<float*>(v_scale),
+                      static_cast<float*>(smooth), static_cast<float*>(scratch),
+                      static_cast<hipStream_t>(stream)),
+                  "quantize launch");
+}
+
+int wan_attn8_fwd_quantized(const void* q_codes, const void* q_scale, const void* k_codes,
+                            const void* k_scale, const void* v_codes, const void* v_scale, void* o,
+                            int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                            int64_t head_dim, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !o) return WAN_ATTN_EINVAL;
+  const void* ptrs[] = {q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  return from_hip(wan::launch_attn8_fwd(static_cast<const int8_t*>(q_codes),
+                                        static_cast<const float*>(q_scale),
+                                        static_cast<const int8_t*>(k_codes),
+                                        static_cast<const float*>(k_scale),
+                                        static_cast<const uint8_t*>(v_codes),
+                                        static_cast<const float*>(v_scale), o, sh,
+                                        static_cast<hipStream_t>(stream)),
+                  "8-bit attention launch");
+}
+
+int wan_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch,
+                 int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim, int dtype,
+                 void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  if (dtype != WAN_ATTN_BF16 && dtype != WAN_ATTN_INT8_FP8) return WAN_ATTN_EINVAL;
+  rc = check_qkvo(q, k, v, o, batch, heads, s_q, s_kv);
+  if (rc) return rc;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  WAN_LOG("fwd dtype=%d b=%lld H=%lld s_q=%lld s_kv=%lld", dtype, (long long)batch,
+          (long long)heads, (long long)s_q, (long long)s_kv);
+  if (dtype == WAN_ATTN_BF16) return from_hip(wan::launch_attn_bf16(q, k, v, o, sh, st), "bf16 attention launch");
+
+  // 8-bit: quantise into stream-ordered scratch, attend, release the scratch on the stream.
+  hipMemPool_t pool;
+  rc = pool_for_current_device(&pool);
+  if (rc) return rc;
+  const Attn8Layout L = attn8_layout(batch, heads, s_q, s_kv);
+  if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) return WAN_ATTN_ENOMEM;
+  void* ws = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&ws, L.total, pool, st);
+  if (e != hipSuccess || ws == nullptr) {
+    WAN_LOG("scratch allocation of %zu bytes failed", L.total);
+    return WAN_ATTN_ENOMEM;
+  }
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  int8_t* qc = reinterpret_cast<int8_t*>(base + L.q_codes);
+  int8_t* kc = reinterpret_cast<int8_t*>(base + L.k_codes);
+  uint8_t* vc = base + L.v_codes;
+  float* qs = reinterpret_cast<float*>(base + L.q_scale);
+  float* kscale = reinterpret_cast<float*>(base + L.k_scale);
+  float* vscale = reinterpret_cast<float*>(base + L.v_scale);
+  float* sm = reinterpret_cast<float*>(base + L.smooth);
+  float* cm = reinterpret_cast<float*>(base + L.chan_max);
+  rc = from_hip(wan::launch_attn8_quantize(q, k, v, sh, qc, qs, kc, kscale, vc, vscale, sm, cm, st),
+                "quantize launch");
+  if (!rc)
+    rc = from_hip(wan::launch_attn8_fwd(qc, qs, kc, kscale, vc, vscale, o, sh, st),
+                  "8-bit attention launch");
+  hipError_t fe = hipFreeAsync(ws, st);
+  if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
+  return rc;
+}
+
+}  // extern "C"
