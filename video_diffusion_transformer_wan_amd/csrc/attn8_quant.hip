@@ -77,8 +77,9 @@ __global__ __launch_bounds__(kThreads) void chan_max_kernel(const uint16_t* q, c
   }
 }
 
+// sqrtf (not __fsqrt_rn, which maps to the bare v_sqrt_f32) is the correctly rounded square root
 __device__ __forceinline__ float smooth_factor(float aq, float ak) {
-  return (aq > 0.0f && ak > 0.0f) ? __fsqrt_rn(__fdiv_rn(ak, aq)) : 1.0f;
+  return (aq > 0.0f && ak > 0.0f) ? sqrtf(__fdiv_rn(ak, aq)) : 1.0f;
 }
 
 // One 64-token block of Q (blockIdx.z = 0) or K (1): scale by smooth (Q) or 1/smooth (K), block
