@@ -145,6 +145,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
@@ -152,6 +154,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_mib:
+        # a plain copy of known size: reads and writes exactly copy_mib MiB per dispatch
+        x = torch.ones(args.copy_mib << 18, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(max(1, args.steps)):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_mib": args.copy_mib, "dispatches": max(1, args.steps)}), flush=True)
+        return
     import video_diffusion_transformer_wan_amd as wan
     import wan_inputs
     if not os.path.exists(wan.LIB_PATH):

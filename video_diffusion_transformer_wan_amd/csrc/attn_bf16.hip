@@ -47,7 +47,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 
 constexpr int kBN = 64;                     // keys per tile
 constexpr int kKBytes = kBN * kHeadDim * 2;      // K tile, 16 KB
-constexpr int kVBytes = kHeadDim * kBN * 2;      // V^T tile, 16 KB
+constexpr int kVBytes = kBN * kHeadDim * 2;      // V tile, 16 KB
 constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr float kNeg = -1.0e30f;            // masked score (finite: keeps inf - inf out)
 constexpr float kLazyLog2 = 8.0f;           // move the running max only past this growth
@@ -70,17 +70,6 @@ struct Params {
 __device__ __forceinline__ int swap23(int x) {
   return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
-// K tile: 64 rows (keys, permuted by swap23) x 256 B; 16-byte chunk j of row r sits at j ^ (r%16)
-__device__ __forceinline__ int k_off(int r, int j) { return r * 256 + ((j ^ (r & 15)) << 4); }
-// V^T tile: 128 rows (channels) x 128 B (64 keys); chunk j (keys 8j..8j+7) sits at j ^ ((d/2)%8)
-__device__ __forceinline__ int vt_off(int d, int j) { return d * 128 + ((j ^ ((d >> 1) & 7)) << 4); }
-
-__device__ __forceinline__ unsigned pack_lo(unsigned a, unsigned b) {   // {a.lo16, b.lo16}
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ unsigned pack_hi(unsigned a, unsigned b) {   // {a.hi16, b.hi16}
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
 
 __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
   bf16x2_t r;
@@ -89,13 +78,55 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
+constexpr short kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters untouched
+
+// Buffer resource over [base, base + bytes); loads past the end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcFlags);
+}
+
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// The V^T operands of one 16-key step t (keys 16t .. 16t+15) for the four 32-channel blocks:
+// two transposed 64-bit LDS reads per block (keys +0..3 and +4..7 of the lane's half).  Written
+// as one asm block that waits for its own reads, so the compiler never sees an output register
+// before its data has landed, and the reads are not held back behind the in-flight direct loads
+// of the next tile (which write the other LDS stage).
+__device__ __forceinline__ void read_v_step(unsigned vs_lds, const int (&v_rd)[4], int t, u32x2_t (&r)[8]) {
+  const unsigned a0 = vs_lds + v_rd[0] + 4096 * t, a1 = vs_lds + v_rd[1] + 4096 * t;
+  const unsigned a2 = vs_lds + v_rd[2] + 4096 * t, a3 = vs_lds + v_rd[3] + 4096 * t;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %2, %9\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %4, %10\n\t"
+      "ds_read_b64_tr_b16 %5, %10 offset:1024\n\t"
+      "ds_read_b64_tr_b16 %6, %11\n\t"
+      "ds_read_b64_tr_b16 %7, %11 offset:1024\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
 // kWaves waves per workgroup, each owning kQB blocks of 32 query rows.
 template <int kWaves, int kQB>
 __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Params p) {
-  constexpr int kThreads = kWaves * 64;
   constexpr int kBM = kWaves * 32 * kQB;
-  static_assert(kWaves == 4 || kWaves == 8, "loader split assumes 4 or 8 waves");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kStageBytes];
+  static_assert(kWaves == 8, "K/V tile loads are split over exactly 8 waves");
+  // [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
+  // natural order, 16-byte chunks XOR-swizzled by 4 * (key % 4), read back transposed.
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kStageBytes];
 
   // XCD-aware numbering: workgroup w runs on XCD w % 8; give each XCD a contiguous range.
   const int w = blockIdx.x;
@@ -108,82 +139,71 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Par
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  const int64_t tok_stride = (int64_t)p.heads * kHeadDim;   // elements between tokens
-  const uint16_t* qbase = p.q + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
-  const uint16_t* kbase = p.k + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim;
-  const uint16_t* vbase = p.v + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim;
+  const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
+  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
   uint16_t* obase = p.o + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
+  const int64_t kv_bytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
 
   // ---- Q^T operand: lane holds query row (l32) of block qb, channels 16c + 8h .. +7
+  // (rows past s_q read as zeros and are never stored)
   bf16x8_t qf[kQB][8];
   const int q0 = qt * kBM + wv * (32 * kQB);
+  {
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(qbase + q0 * stride, (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2);
 #pragma unroll
-  for (int qb = 0; qb < kQB; ++qb) {
-    // rows past s_q read the last row; their results are never stored
-    const int row = min(q0 + qb * 32 + l32, p.s_q - 1);
-    const uint16_t* src = qbase + (int64_t)row * tok_stride + 8 * h;
+    for (int qb = 0; qb < kQB; ++qb)
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      qf[qb][c] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src + 16 * c));
+      for (int c = 0; c < 8; ++c)
+        qf[qb][c] = __builtin_bit_cast(
+            bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)((qb * 32 + l32) * stride + 32 * c + 16 * h), 0, 0));
   }
 
-  // ---- global -> register staging of one K/V tile (256 threads each for K and for V; with 4
-  // waves every thread does both, with 8 waves waves 0-3 take K and waves 4-7 take V)
-  // K: thread covers rows it*16 + t/16 (it = 0..3), 16-byte chunk t%16
-  // V: thread covers keys 4g..4g+3 (g = t/16) at channels 8s..8s+7 (s = t%16)
-  const int lt = tid & 255;
-  const bool k_loader = kWaves == 4 || tid < 256;
-  const bool v_loader = kWaves == 4 || tid >= 256;
-  const int kr_row = lt >> 4;
-  const int kr_chunk = lt & 15;
-  const int vg = lt >> 4;
-  const int vs = lt & 15;
-  u32x4_t kreg[4], vreg[4];
-
-  auto load_tile = [&](int j) {
-    const int kv0 = j * kBN;
-    if (k_loader) {
+  // ---- per-lane offsets of the direct global -> LDS tile loads: wave wv fills 1 KB blocks
+  // m = 2wv and 2wv+1 of the K tile and of the V tile; lane i writes bytes 16i .. 16i+15.
+  unsigned k_src[2], v_src[2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      // keys past s_kv read the last key: finite values whose scores are masked below
-      const int key = min(kv0 + it * 16 + kr_row, p.s_kv - 1);
-      kreg[it] = *reinterpret_cast<const u32x4_t*>(kbase + (int64_t)key * tok_stride + 8 * kr_chunk);
-    }
-    }
-    if (v_loader) {
+  for (int it = 0; it < 2; ++it) {
+    const int m = 2 * wv + it;
+    const int row = 4 * m + (lane >> 4);
+    const int pch = lane & 15;
+    k_src[it] = (unsigned)(swap23(row) * stride + 16 * (pch ^ (row & 15)));
+    v_src[it] = (unsigned)(row * stride + 16 * (pch ^ ((row & 3) << 2)));
+  }
+  auto issue_tile = [&](int j) {
+    const int64_t off = (int64_t)j * kBN * stride;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, kv_bytes - off);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, kv_bytes - off);
+    unsigned char* st = smem + (j & 1) * kStageBytes;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      // past s_kv: finite values of the last key, weighted by an exact 0
-      const int key = min(kv0 + 4 * vg + r, p.s_kv - 1);
-      vreg[r] = *reinterpret_cast<const u32x4_t*>(vbase + (int64_t)key * tok_stride + 8 * vs);
-    }
+    for (int it = 0; it < 2; ++it) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + 1024 * (2 * wv + it)), 16, k_src[it], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes + 1024 * (2 * wv + it)), 16, v_src[it], 0, 0, 0);
     }
   };
 
-  auto store_tile = [&](unsigned char* ks, unsigned char* vts) {
-    if (k_loader) {
+  // ---- per-lane LDS read offsets
+  // K (A operand of S^T): row l32 (+32 for the second key block), chunk (2c + h) ^ (l32 % 16)
+  int k_rd[8];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int rho = swap23(it * 16 + kr_row);
-      *reinterpret_cast<u32x4_t*>(ks + k_off(rho, kr_chunk)) = kreg[it];
-    }
-    }
-    if (v_loader) {
-    // transpose 4 keys x 8 channels into 8 rows of V^T, 4 keys (8 bytes) each
+  for (int c = 0; c < 8; ++c) k_rd[c] = l32 * 256 + 16 * ((2 * c + h) ^ (l32 & 15));
+  // V (A operand of O^T, transposed read): within each 16-lane group, lane 4r + q addresses key
+  // row r and channels 4q .. 4q+3 of its 16-channel slice; the read hands lane i channel i of
+  // four consecutive keys.
+  int v_rd[4];
+  {
+    const int g = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
+    const int x = 2 * (g & 1) + (q >> 1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int d0 = 8 * vs + 2 * i;
-      u32x2_t lo = {pack_lo(vreg[0][i], vreg[1][i]), pack_lo(vreg[2][i], vreg[3][i])};
-      u32x2_t hi = {pack_hi(vreg[0][i], vreg[1][i]), pack_hi(vreg[2][i], vreg[3][i])};
-      *reinterpret_cast<u32x2_t*>(vts + vt_off(d0, vg >> 1) + ((vg & 1) << 3)) = lo;
-      *reinterpret_cast<u32x2_t*>(vts + vt_off(d0 + 1, vg >> 1) + ((vg & 1) << 3)) = hi;
-    }
-    }
-  };
+    for (int db = 0; db < 4; ++db)
+      v_rd[db] = (8 * (g >> 1) + kq) * 256 + 64 * (db ^ kq) + 16 * x + 8 * (q & 1);
+  }
 
   f32x16_t o[4][kQB];
 #pragma unroll
@@ -201,14 +221,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Par
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   const int n_tiles = (p.s_kv + kBN - 1) / kBN;
-  load_tile(0);
+  issue_tile(0);
 
   for (int j = 0; j < n_tiles; ++j) {
-    unsigned char* ks = smem + (j & 1) * kStageBytes;
-    unsigned char* vts = ks + kKBytes;
-    store_tile(ks, vts);
+    // tile j is in LDS once every wave's loads have landed; the barrier also tells every wave
+    // that tile j-1's buffer is no longer read, so tile j+1 may overwrite it
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
-    if (j + 1 < n_tiles) load_tile(j + 1);
+    if (j + 1 < n_tiles) issue_tile(j + 1);
+    const unsigned char* ks = smem + (j & 1) * kStageBytes;
+    const unsigned vs_lds = lds_addr(ks + kKBytes);
 
     // ---- S^T = K Q^T for the 64 keys of this tile: [key block kb][query block qb]
     f32x16_t s[2][kQB];
@@ -222,7 +244,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Par
     for (int c = 0; c < 8; ++c) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + k_off(32 * kb + l32, 2 * c + h));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c] + 8192 * kb);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[qb][c], s[kb][qb], 0, 0, 0);
@@ -299,9 +321,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Par
                            pk[kb][qb][4 * u + 3]};
         bop[qb] = __builtin_bit_cast(bf16x8_t, x);
       }
+      u32x2_t vt[8];
+      read_v_step(vs_lds, v_rd, t, vt);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(vts + vt_off(32 * db + l32, 2 * t + h));
+        const u32x4_t cat = {vt[2 * db][0], vt[2 * db][1], vt[2 * db + 1][0], vt[2 * db + 1][1]};
+        const bf16x8_t a = __builtin_bit_cast(bf16x8_t, cat);
 #pragma unroll
         for (int qb = 0; qb < kQB; ++qb)
           o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bop[qb], o[db][qb], 0, 0, 0);
@@ -316,7 +341,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void attn_fwd_bf16_kernel(const Par
     const float inv = 1.0f / lt;
     const int row = q0 + qb * 32 + l32;
     if (row < p.s_q) {
-      uint16_t* dst = obase + (int64_t)row * tok_stride + 4 * h;
+      uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
