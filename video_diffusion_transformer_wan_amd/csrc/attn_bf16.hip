@@ -68,7 +68,8 @@ struct Params {
   int s_kv;
   int q_tiles;
   int total;      // q_tiles * batch * heads
-  int per_xcd;    // ceil(total / 8)
+  int per_xcd;    // ceil(total / 8): query tiles handled by each XCD
+  int n_slots;    // workgroups per XCD (gridDim.x / 8)
 };
 
 __device__ __forceinline__ int swap23(int x) {
@@ -97,24 +98,18 @@ __device__ __forceinline__ void pair_values(float x, float& a, float& b) {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Buffer resource over [base, base + bytes); loads past the end return zeros.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int n = bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, (int)kRsrcFlags);
+__device__ __forceinline__ int clamp_bytes(int64_t bytes) {
+  return bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
 }
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, clamp_bytes(bytes), (int)kRsrcFlags);
+}
+
 
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params p) {
   // [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
   // natural order, 16-byte chunks XOR-swizzled by 4 * (key % 4).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
-
-  // XCD-aware numbering: workgroup w runs on XCD w % 8; give each XCD a contiguous range.
-  const int w = blockIdx.x;
-  const int tile = (w & 7) * p.per_xcd + (w >> 3);
-  if (tile >= p.total) return;
-  const int qt = tile % p.q_tiles;
-  const int bh = tile / p.q_tiles;
-  const int bb = bh / p.heads;
-  const int hh = bh - bb * p.heads;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,27 +117,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
   const bool first_group = wv < kWaves / 2;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
-  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
-  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
-  uint16_t* obase = p.o + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
-  const int64_t kv_bytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
   const int n_tiles = (p.s_kv + kBN - 1) / kBN;
-
-  // ---- Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7
-  // (rows past s_q read as zeros and are never stored)
-  bf16x8_t qf[8];
-  const int q0 = qt * kBM + wv * 32;
-  {
-    const __amdgpu_buffer_rsrc_t qr =
-        make_rsrc(qbase + q0 * stride, (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      qf[c] = __builtin_bit_cast(
-          bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
-  }
 
   // ---- direct global -> LDS tile loads: wave wv fills 1 KB blocks 2wv and 2wv+1 of the K tile
   // and of the V tile; lane i writes bytes 16i .. 16i+15 of its block.
@@ -155,17 +131,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     k_src[it] = (unsigned)(swap23(row) * stride + 16 * (pch ^ (row & 15)));
     v_src[it] = (unsigned)(row * stride + 16 * (pch ^ ((row & 3) << 2)));
   }
-  auto issue_tile = [&](int j) {
-    const int64_t off = (int64_t)j * kBN * stride;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, kv_bytes - off);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, kv_bytes - off);
-    unsigned char* st = smem + (j % kStages) * kStageBytes;
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + 1024 * (2 * wv + it)), 16, k_src[it], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes + 1024 * (2 * wv + it)), 16, v_src[it], 0, 0, 0);
-    }
-  };
 
   // ---- per-lane LDS read offsets
   // K (A operand of S^T): row l32 (+32 for the second key block), chunk (2c + h) ^ (l32 % 16)
@@ -183,153 +148,195 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     for (int db = 0; db < 4; ++db)
       v_rd[db] = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * (db ^ kq) + 16 * x + 8 * (q & 1);
   }
-
-  f32x16_t o[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m = kNeg, l = 0.0f;
-  f32x16_t s[2];          // S^T of the newest tile, per 32-key block
-  unsigned pk[2][8];      // bf16 P^T of the tile awaiting its PV product (pairs of S^T registers)
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // MFMA half-step: S^T of tile j (if any), then the PV product of tile j-1 (if any).
-  auto mfma_phase = [&](int j) {
-    if (j < n_tiles) {
-      // K operands are read one step ahead of the MFMAs that use them; the scheduling barriers
-      // keep the compiler from hoisting every read of the phase (and its registers) to the top.
-      const unsigned char* ks = smem + (j % kStages) * kStageBytes;
-      bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0]);
-      bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0] + 8192);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        bf16x8_t n0 = a0, n1 = a1;
-        if (c < 7) {
-          n0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1]);
-          n1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1] + 8192);
-        }
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[1], 0, 0, 0);
-        a0 = n0;
-        a1 = n1;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (j >= 1) {
-      const unsigned char* st = smem + ((j - 1) % kStages) * kStageBytes;
-      auto read_v = [&](int t, bf16x8_t (&a)[4]) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const unsigned char* vp = st + v_rd[db] + 4096 * t;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
-          const i16x4_t cat[2] = {lo, hi};
-          a[db] = __builtin_bit_cast(bf16x8_t, cat);
-        }
-      };
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        bf16x8_t va[4];
-        read_v(t, va);
-        // keys 16t .. 16t+15: S^T registers 8u .. 8u+7 of key block t/2
-        const int kb = t >> 1, u = t & 1;
-        const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
-        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], bop, o[db], 0, 0, 0);
-      }
-    }
-    // this wave's loads of tile j+1 (issued at the start of its previous softmax half-step) must
-    // have landed before the barrier that ends this half-step
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  };
+  // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes query tiles slot, slot +
+  // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
+  // query tiles of one head in lockstep and read each K/V tile through their shared L2.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
+    const int tile = xcd * p.per_xcd + t_local;
+    if (tile >= p.total) break;
+    const int qt = tile % p.q_tiles;
+    const int bh = tile / p.q_tiles;
+    const int bb = bh / p.heads;
+    const int hh = bh - bb * p.heads;
 
-  // VALU half-step: this wave's share of the loads of tile j+2, then the online softmax of tile j
-  // (its S^T is in s), leaving bf16 P^T in pk.
-  auto softmax_phase = [&](int j) {
-    if (j + 2 < n_tiles) issue_tile(j + 2);
-    const int kv0 = j * kBN;
-    if (kv0 + kBN > p.s_kv) {   // keys past the end of the sequence contribute nothing
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + swap23(32 * kb + 8 * (r >> 2) + 4 * h + (r & 3));
-          if (key >= p.s_kv) s[kb][r] = kNeg;
-        }
-    }
-    float mx = m;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
-    float ma, mb;
-    pair_values(mx, ma, mb);
-    const float mnew = __builtin_fmaxf(ma, mb);
-    if (__any((mnew - m) * kScaleLog2 > kLazyLog2)) {
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * kScaleLog2);
-      m = mnew;
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-    }
-    const float mc = m * kScaleLog2;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kScaleLog2, -mc));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], kScaleLog2, -mc));
-        const unsigned pp = cvt_pk_bf16(p0, p1);
-        pk[kb][r >> 1] = pp;
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l, false);
-      }
-  };
+    const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+    uint16_t* obase = p.o + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
+    const int64_t kv_bytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
 
-  // Schedule (B_k = k-th workgroup barrier).  Every wave runs the same sequence
-  //   MFMA(j) | barrier | softmax(j) | barrier   for j = 0 .. n-1, then the PV product of tile n-1,
-  // but waves 4-7 enter it one barrier later than waves 0-3, so between consecutive barriers one
-  // group issues MFMAs while the other is on the VALU.  Tile t is loaded into stage t % 4 at the
-  // start of softmax(t-2) -- after B_{2t-3} (group 1) or B_{2t-2} (group 2), both after the last
-  // read of tile t-4 in group 2's MFMA(t-3) -- and waited for at the end of MFMA(t-1), before the
-  // barrier B_{2t} after which group 1 reads it.
-  issue_tile(0);
-  if (n_tiles > 1) issue_tile(1);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  barrier();
-  if (!first_group) barrier();
-  for (int j = 0; j < n_tiles; ++j) {
-    mfma_phase(j);
-    barrier();
-    softmax_phase(j);
-    barrier();
-  }
-  mfma_phase(n_tiles);
-  if (first_group) barrier();
+    // ---- Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7
+    // (rows past s_q read as zeros and are never stored)
+    bf16x8_t qf[8];
+    const int q0 = qt * kBM + wv * 32;
+    {
+      const __amdgpu_buffer_rsrc_t qr =
+          make_rsrc(qbase + q0 * stride, (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        qf[c] = __builtin_bit_cast(
+            bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
+    }
 
-  // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row
-  float la, lb;
-  pair_values(l, la, lb);
-  const float inv = 1.0f / (la + lb);
-  const int row = q0 + l32;
-  if (row < p.s_q) {
-    uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
+    auto issue_tile = [&](int j) {
+      const int64_t off = (int64_t)j * kBN * stride;
+      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, kv_bytes - off);
+      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, kv_bytes - off);
+      unsigned char* st = smem + (j % kStages) * kStageBytes + 2048 * wv;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st), 16, k_src[0], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + 1024), 16, k_src[1], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes), 16, v_src[0], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes + 1024), 16, v_src[1], 0, 0, 0);
+    };
+
+    f32x16_t o[4];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                     cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
+      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+    float m = kNeg, l = 0.0f;
+    f32x16_t s[2];          // S^T of the newest tile, per 32-key block
+    unsigned pk[2][8];      // bf16 P^T of the tile awaiting its PV product (pairs of S^T registers)
+
+    // MFMA half-step: S^T of tile j (if any), then the PV product of tile j-1 (if any).
+    auto mfma_phase = [&](int j) {
+      if (j < n_tiles) {
+        // K operands are read one step ahead of the MFMAs that use them; the scheduling
+        // barriers keep the compiler from hoisting every read of the phase to the top.
+        const unsigned char* ks = smem + (j % kStages) * kStageBytes;
+        bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0]);
+        bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0] + 8192);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          bf16x8_t n0 = a0, n1 = a1;
+          if (c < 7) {
+            n0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1]);
+            n1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1] + 8192);
+          }
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[1], 0, 0, 0);
+          a0 = n0;
+          a1 = n1;
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      if (j >= 1) {
+        const unsigned char* st = smem + ((j - 1) % kStages) * kStageBytes;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bf16x8_t va[4];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const unsigned char* vp = st + v_rd[db] + 4096 * t;
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
+            const i16x4_t cat[2] = {lo, hi};
+            va[db] = __builtin_bit_cast(bf16x8_t, cat);
+          }
+          // keys 16t .. 16t+15: S^T registers 8u .. 8u+7 of key block t/2
+          const int kb = t >> 1, u = t & 1;
+          const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+          const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], bop, o[db], 0, 0, 0);
+        }
+      }
+      // this wave's loads of tile j+1 (issued at the start of its previous softmax half-step)
+      // must have landed before the barrier that ends this half-step
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    };
+
+    // VALU half-step: this wave's share of the loads of tile j+2, then the online softmax of
+    // tile j (its S^T is in s), leaving bf16 P^T in pk.
+    auto softmax_phase = [&](int j) {
+      if (j + 2 < n_tiles) issue_tile(j + 2);
+      const int kv0 = j * kBN;
+      if (kv0 + kBN > p.s_kv) {   // keys past the end of the sequence contribute nothing
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + swap23(32 * kb + 8 * (r >> 2) + 4 * h + (r & 3));
+            if (key >= p.s_kv) s[kb][r] = kNeg;
+          }
+      }
+      float mx = m;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+      float ma, mb;
+      pair_values(mx, ma, mb);
+      const float mnew = __builtin_fmaxf(ma, mb);
+      if (__any((mnew - m) * kScaleLog2 > kLazyLog2)) {
+        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * kScaleLog2);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      const float mc = m * kScaleLog2;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kScaleLog2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], kScaleLog2, -mc));
+          const unsigned pp = cvt_pk_bf16(p0, p1);
+          pk[kb][r >> 1] = pp;
+          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l, false);
+        }
+    };
+
+    // Schedule (B_k = k-th workgroup barrier of this query tile).  Every wave runs the same
+    // sequence  MFMA(j) | barrier | softmax(j) | barrier  for j = 0 .. n-1, then the PV product
+    // of tile n-1, but waves 4-7 enter it one barrier later than waves 0-3, so between
+    // consecutive barriers one group issues MFMAs while the other is on the VALU.  Tile t is
+    // loaded into stage t % 4 at the start of softmax(t-2) -- after B_{2t-3} (group 1) or
+    // B_{2t-2} (group 2), both after the last read of tile t-4 in group 2's MFMA(t-3) -- and
+    // waited for at the end of MFMA(t-1), before the barrier B_{2t} after which group 1 reads it.
+    issue_tile(0);
+    if (n_tiles > 1) issue_tile(1);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    barrier();
+    if (!first_group) barrier();
+    for (int j = 0; j < n_tiles; ++j) {
+      mfma_phase(j);
+      barrier();
+      softmax_phase(j);
+      barrier();
+    }
+    mfma_phase(n_tiles);
+    if (first_group) barrier();
+    barrier();   // every wave is done with the LDS ring before the next tile's loads
+
+    // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row
+    float la, lb;
+    pair_values(l, la, lb);
+    const float inv = 1.0f / (la + lb);
+    const int row = q0 + l32;
+    if (row < p.s_q) {
+      uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                       cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
+        }
+    }
   }
 }
 
@@ -348,7 +355,18 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   p.q_tiles = (int)ceil_div(sh.s_q, kBM);
   p.total = (int)(p.q_tiles * sh.batch * sh.heads);
   p.per_xcd = (int)ceil_div(p.total, 8);
-  const dim3 grid((unsigned)(8 * p.per_xcd));
+  // one workgroup per CU (the LDS ring and the registers allow no second one)
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n >= 8)
+      cus = n;
+    else
+      cus = 256;
+  }
+  p.n_slots = (int)(p.per_xcd < cus / 8 ? p.per_xcd : cus / 8);
+  const dim3 grid((unsigned)(8 * p.n_slots));
   hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
