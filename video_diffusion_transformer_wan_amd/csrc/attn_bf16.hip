@@ -29,6 +29,8 @@
 //  * Workgroups are numbered so that the 32 CUs of one XCD work on consecutive query tiles of the
 //    same head and share its K/V stream in their L2.
 
+#include <type_traits>
+
 #include "wan_attn_internal.h"
 
 namespace wan {
@@ -133,20 +135,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
   }
 
   // ---- per-lane LDS read offsets
-  // K (A operand of S^T): row l32 (+32 for the second key block), chunk (2c + h) ^ (l32 % 16)
-  int k_rd[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) k_rd[c] = l32 * 256 + 16 * ((2 * c + h) ^ (l32 & 15));
+  // K (A operand of S^T): row l32 (+32 for the second key block), 16-byte chunk
+  // (2c + h) ^ (l32 % 16), i.e. byte offset k_rd0 ^ 32c (bits 5-7 carry c ^ ((l32 / 2) % 8))
+  const int k_rd0 = l32 * 256 + 16 * ((h ^ l32) & 1) + 32 * ((l32 >> 1) & 7);
   // V (A operand of O^T, transposed read): within each 16-lane group, lane 4r + q addresses key
   // row r and channels 4q .. 4q+3 of its 16-channel slice; the read hands lane i channel i of
   // four consecutive keys.  Rows 16t + 8h + 4e (e = 0, 1) give the 8 keys of one MFMA.
-  int v_rd[4];
+  // Offset of channel block db: v_rd0 ^ 64db (bits 6-7 carry db ^ (row % 4)).
+  int v_rd0;
   {
     const int g = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
     const int x = 2 * (g & 1) + (q >> 1);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-      v_rd[db] = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * (db ^ kq) + 16 * x + 8 * (q & 1);
+    v_rd0 = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * kq + 16 * x + 8 * (q & 1);
   }
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -202,58 +202,73 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     f32x16_t s[2];          // S^T of the newest tile, per 32-key block
     unsigned pk[2][8];      // bf16 P^T of the tile awaiting its PV product (pairs of S^T registers)
 
-    // MFMA half-step: S^T of tile j (if any), then the PV product of tile j-1 (if any).
-    auto mfma_phase = [&](int j) {
-      if (j < n_tiles) {
-        // K operands are read one step ahead of the MFMAs that use them; the scheduling
-        // barriers keep the compiler from hoisting every read of the phase to the top.
-        const unsigned char* ks = smem + (j % kStages) * kStageBytes;
-        bf16x8_t a0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0]);
-        bf16x8_t a1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[0] + 8192);
+    // MFMA half-step: S^T of tile j (kQK), then the PV product of tile j-1 (kPV), as one stream
+    // of 8 steps of 4 MFMAs (4 S^T steps over 32 channels each, 4 PV steps over 16 keys each).
+    // The LDS operands of step i+1 are read while step i issues its MFMAs (two operand sets);
+    // the scheduling barriers keep that order, and the register footprint, as written.
+    auto mfma_phase = [&](int j, auto qk_tag, auto pv_tag) {
+      constexpr bool kQK = decltype(qk_tag)::value;
+      constexpr bool kPV = decltype(pv_tag)::value;
+      const unsigned char* ks = smem + (j % kStages) * kStageBytes;
+      const unsigned char* vst = smem + ((j + kStages - 1) % kStages) * kStageBytes;
+      // raised issue priority: the SIMD's other wave is in its softmax half-step, and its VALU
+      // stream would otherwise delay these MFMAs
+      __builtin_amdgcn_s_setprio(3);
+      constexpr int kFirst = kQK ? 0 : 4;
+      constexpr int kSteps = kPV ? 8 : 4;
+      bf16x8_t ring[2][4];
+      auto read_step = [&](int i, bf16x8_t (&f)[4]) {
+        if (i < 4) {   // channels 32i .. 32i+31 (c = 2i, 2i+1) of both 32-key blocks
+          const int o0 = k_rd0 ^ (64 * i), o1 = k_rd0 ^ (64 * i + 32);
+          f[0] = *reinterpret_cast<const bf16x8_t*>(ks + o0);
+          f[1] = *reinterpret_cast<const bf16x8_t*>(ks + o0 + 8192);
+          f[2] = *reinterpret_cast<const bf16x8_t*>(ks + o1);
+          f[3] = *reinterpret_cast<const bf16x8_t*>(ks + o1 + 8192);
+        } else {       // keys 16t .. 16t+15 of the four 32-channel blocks, t = i - 4
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const unsigned char* vp = vst + (v_rd0 ^ (64 * db)) + 4096 * (i - 4);
+            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
+            const i16x4_t cat[2] = {lo, hi};
+            f[db] = __builtin_bit_cast(bf16x8_t, cat);
+          }
+        }
+      };
+      if constexpr (kQK) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          bf16x8_t n0 = a0, n1 = a1;
-          if (c < 7) {
-            n0 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1]);
-            n1 = *reinterpret_cast<const bf16x8_t*>(ks + k_rd[c + 1] + 8192);
-          }
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[c], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[c], s[1], 0, 0, 0);
-          a0 = n0;
-          a1 = n1;
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
-      if (j >= 1) {
-        const unsigned char* st = smem + ((j - 1) % kStages) * kStageBytes;
+      read_step(kFirst, ring[0]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          bf16x8_t va[4];
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const unsigned char* vp = st + v_rd[db] + 4096 * t;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
-            const i16x4_t cat[2] = {lo, hi};
-            va[db] = __builtin_bit_cast(bf16x8_t, cat);
-          }
+      for (int i = kFirst; i < kSteps; ++i) {
+        const int cur = (i - kFirst) & 1;
+        if (i + 1 < kSteps) read_step(i + 1, ring[cur ^ 1]);
+        if (i < 4) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][0], qf[2 * i], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][1], qf[2 * i], s[1], 0, 0, 0);
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][2], qf[2 * i + 1], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][3], qf[2 * i + 1], s[1], 0, 0, 0);
+        } else {
           // keys 16t .. 16t+15: S^T registers 8u .. 8u+7 of key block t/2
-          const int kb = t >> 1, u = t & 1;
+          const int t = i - 4, kb = t >> 1, u = t & 1;
           const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
           const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
 #pragma unroll
           for (int db = 0; db < 4; ++db)
-            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db], bop, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][db], bop, o[db], 0, 0, 0);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // this wave's loads of tile j+1 (issued at the start of its previous softmax half-step)
       // must have landed before the barrier that ends this half-step
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     };
+    const std::true_type yes{};
+    const std::false_type no{};
 
     // VALU half-step: this wave's share of the loads of tile j+2, then the online softmax of
     // tile j (its S^T is in s), leaving bf16 P^T in pk.
@@ -311,13 +326,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     barrier();
     if (!first_group) barrier();
-    for (int j = 0; j < n_tiles; ++j) {
-      mfma_phase(j);
-      barrier();
-      softmax_phase(j);
-      barrier();
+    mfma_phase(0, yes, no);
+    barrier();
+    softmax_phase(0);
+    barrier();
+    if (n_tiles > 1) {
+      int j = 1;
+      do {
+        mfma_phase(j, yes, yes);
+        barrier();
+        softmax_phase(j);
+        barrier();
+      } while (++j < n_tiles);
     }
-    mfma_phase(n_tiles);
+    mfma_phase(n_tiles, no, yes);
     if (first_group) barrier();
     barrier();   // every wave is done with the LDS ring before the next tile's loads
 
