@@ -49,8 +49,36 @@ def test_batches_and_heads(b, H, s_q, s_kv):
     assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS, (rel, mx)
 
 
+def _growing_keys(s_q, s_kv, seed, growth, q_scale_rows=0, q_scale=1.0):
+    """Q, K, V ~ N(0, 1) with every key from the second 64-key block on multiplied by growth
+    (and the first q_scale_rows query rows by q_scale): scores after the first tile outgrow the
+    reference maximum the kernel takes from it."""
+    q, k, v = wan_inputs.random_qkv(1, 2, s_q, s_kv, seed, device="cuda")
+    k = k.clone()
+    k[:, 64:] = (k[:, 64:].float() * growth).to(torch.bfloat16)
+    if q_scale_rows:
+        q = q.clone()
+        q[:, :q_scale_rows] = (q[:, :q_scale_rows].float() * q_scale).to(torch.bfloat16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("growth,q_rows", [(6.0, 0), (40.0, 0), (40.0, 100)])
+def test_scores_outgrowing_the_first_tile(growth, q_rows):
+    # growth 6: later scores exceed the first tile's maximum by up to ~2^30 in P, which the fixed
+    # reference absorbs; growth 40: P would overflow (row sums past 2^64), so the query tiles take
+    # the exact path (row max sweep, then softmax against it); q_rows: only some rows overflow
+    print(f"growing keys x{growth}, {q_rows} damped rows", flush=True)
+    q, k, v = _growing_keys(300, 1000, seed=91, growth=growth, q_scale_rows=q_rows, q_scale=0.02)
+    out = wan.attention(q, k, v)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    assert np.isfinite(got).all()
+    rel, mx, _ = metrics(got, oracle.attention(to_np(q), to_np(k), to_np(v)))
+    assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS, (rel, mx)
+
+
 def test_large_logits_keep_accuracy():
-    # Q, K ~ N(0, 9) make score spreads of tens: exercises the rescale of the running maximum
+    # Q, K ~ N(0, 9) make score spreads of tens, far above the first tile's maximum
     q, k, _ = wan_inputs.random_qkv(1, 2, 300, 2000, seed=77, sigma=3.0, device="cuda")
     _, _, v = wan_inputs.random_qkv(1, 2, 300, 2000, seed=78, device="cuda")
     out = wan.attention(q, k, v)

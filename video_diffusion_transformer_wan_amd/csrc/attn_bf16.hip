@@ -3,8 +3,8 @@
 // Computes O = softmax(Q K^T / sqrt(128)) V per (batch, head), non-causal and unmasked: the full
 // spatio-temporal self-attention of a Wan DiT block and its umT5 cross-attention ("Wan 2.1:
 // VBench 86.22% ..." explainer of the Wan technical report, sections "先看现象" and
-// "干预与形式化").  The result is reached by a tiled online softmax over 64-key blocks, exact in
-// real arithmetic (a re-association of the definition).
+// "干预与形式化").  The result is reached by a tiled softmax over 64-key blocks against a fixed
+// per-row reference max, exact in real arithmetic (a re-association of the definition).
 //
 // Design (one workgroup = 8 waves = 256 query rows of one (batch, head); 1 workgroup per CU):
 //  * The products run transposed so that no operand needs a cross-lane shuffle:
@@ -12,7 +12,7 @@
 //      O^T += V^T P^T (A = V^T from LDS via transposing reads, B = P^T straight from S^T)
 //    With v_mfma_f32_32x32x16_bf16 every lane owns one query row (lane % 32) of its wave's
 //    32 rows, and lanes l and l+32 split the keys.  Row max / row sum are in-lane reductions
-//    plus one v_permlane32_swap, and the per-row rescale of O multiplies a lane's own registers.
+//    plus one v_permlane32_swap.
 //  * K rows sit in LDS with bits 2 and 3 of the key index swapped, which makes the 8 P values a
 //    lane feeds to one PV MFMA belong to 8 consecutive keys.  V stays in natural [key][channel]
 //    order and ds_read_b64_tr_b16 hands each lane 4 consecutive keys of one channel.
@@ -22,10 +22,14 @@
 //    half-step one group issues MFMAs (S^T of tile j and the PV product of tile j-1) while the
 //    other runs the softmax of its tile on the VALU; a workgroup barrier between half-steps keeps
 //    the two groups in opposite phases, so the matrix cores and the VALUs stay busy together.
-//  * Softmax in the exp2 domain with the scale folded in (one FMA + one v_exp_f32 per score); the
-//    running max is only moved (and O rescaled) when some row's max grew by more than 2^8, since
-//    exponents against a stale max stay exact up to that factor; row sums come from the
-//    bf16-rounded P through v_dot2 so numerator and denominator see the same weights.
+//  * Softmax in the exp2 domain with the scale folded in (one FMA + one v_exp_f32 per score),
+//    against a reference max per row that stays fixed for the whole sweep over the keys: the
+//    max of the row's first 64 scores.  Softmax does not depend on the constant subtracted, so
+//    the only risk is that a later, much larger score overflows P; then the row sum exceeds
+//    2^64 (or is infinite), and the query tile is swept again -- once for the true row max
+//    (S^T only), once for the result.  The loop carries no running max, no vote and no
+//    rescaling of O.  Row sums come from the bf16-rounded P through v_dot2 so numerator and
+//    denominator see the same weights.
 //  * Workgroups are numbered so that the 32 CUs of one XCD work on consecutive query tiles of the
 //    same head and share its K/V stream in their L2.
 
@@ -54,7 +58,9 @@ constexpr int kVBytes = kBN * kHeadDim * 2;      // V tile, 16 KB
 constexpr int kStageBytes = kKBytes + kVBytes;
 constexpr int kStages = 4;
 constexpr float kNeg = -1.0e30f;            // masked score (finite: keeps inf - inf out)
-constexpr float kLazyLog2 = 8.0f;           // move the running max only past this growth
+// a row sum above this (P of some key above 2^64 / s_kv) sends the query tile to the exact
+// two-sweep path
+constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 // log2(e) / sqrt(128): scores go straight into exp2
 constexpr float kScaleLog2 = 0.12751743082459868f;
 constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
@@ -107,12 +113,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, clamp_bytes(bytes), (int)kRsrcFlags);
 }
 
+// [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
+// natural order, 16-byte chunks XOR-swizzled by 4 * (key % 4).
+__shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
+__shared__ int redo_flag[kWaves];
 
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params p) {
-  // [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
-  // natural order, 16-byte chunks XOR-swizzled by 4 * (key % 4).
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
-
+// Attention of one query tile (256 rows of one (batch, head)), run by the whole workgroup.
+// kExact = false: one sweep against the max of the first 64 keys; writes O and returns false,
+// or returns true (and writes nothing) when some row sum of the tile passed 2^64.
+// kExact = true: one sweep for the row maxima, one softmax sweep against them; writes O.
+template <bool kExact>
+__device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -149,15 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     v_rd0 = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * kq + 16 * x + 8 * (q & 1);
   }
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes query tiles slot, slot +
-  // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
-  // query tiles of one head in lockstep and read each K/V tile through their shared L2.
-  const int xcd = blockIdx.x & 7;
-  const int slot = blockIdx.x >> 3;
-  for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
-    const int tile = xcd * p.per_xcd + t_local;
-    if (tile >= p.total) break;
+  {
     const int qt = tile % p.q_tiles;
     const int bh = tile / p.q_tiles;
     const int bb = bh / p.heads;
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
             bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
     }
 
-    auto issue_tile = [&](int j) {
+    auto issue_tile = [&](int j) __attribute__((always_inline)) {
       const int64_t off = (int64_t)j * kBN * stride;
       const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, kv_bytes - off);
       const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, kv_bytes - off);
@@ -194,11 +197,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     };
 
     f32x16_t o[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-    float m = kNeg, l = 0.0f;
+    float m = kNeg, l = 0.0f;   // reference max of the lane's query row, lane's part of the row sum
+    float m_run = kNeg;         // max-only sweep: largest score the lane has seen
     f32x16_t s[2];          // S^T of the newest tile, per 32-key block
     unsigned pk[2][8];      // bf16 P^T of the tile awaiting its PV product (pairs of S^T registers)
 
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     // of 8 steps of 4 MFMAs (4 S^T steps over 32 channels each, 4 PV steps over 16 keys each).
     // The LDS operands of step i+1 are read while step i issues its MFMAs (two operand sets);
     // the scheduling barriers keep that order, and the register footprint, as written.
-    auto mfma_phase = [&](int j, auto qk_tag, auto pv_tag) {
+    auto mfma_phase = [&](int j, auto qk_tag, auto pv_tag) __attribute__((always_inline)) {
       constexpr bool kQK = decltype(qk_tag)::value;
       constexpr bool kPV = decltype(pv_tag)::value;
       const unsigned char* ks = smem + (j % kStages) * kStageBytes;
@@ -270,12 +270,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     const std::true_type yes{};
     const std::false_type no{};
 
-    // VALU half-step: this wave's share of the loads of tile j+2, then the online softmax of
-    // tile j (its S^T is in s), leaving bf16 P^T in pk.
-    auto softmax_phase = [&](int j) {
-      if (j + 2 < n_tiles) issue_tile(j + 2);
+    // keys past the end of the sequence (last tile only) get a score that exp2 turns into 0
+    auto mask_tile = [&](int j) __attribute__((always_inline)) {
       const int kv0 = j * kBN;
-      if (kv0 + kBN > p.s_kv) {   // keys past the end of the sequence contribute nothing
+      if (kv0 + kBN > p.s_kv) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -284,22 +282,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
             if (key >= p.s_kv) s[kb][r] = kNeg;
           }
       }
-      float mx = m;
+    };
+
+    // VALU half-step: this wave's share of the loads of tile j+2, then the softmax of tile j
+    // (its S^T is in s) against the reference max, leaving bf16 P^T in pk.  set_ref: tile j = 0
+    // of the first sweep, whose row max becomes the reference.
+    auto softmax_phase = [&](int j, bool set_ref) __attribute__((always_inline)) {
+      if (j + 2 < n_tiles) issue_tile(j + 2);
+      mask_tile(j);
+      if (set_ref) {
+        float mx = kNeg;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
-      float ma, mb;
-      pair_values(mx, ma, mb);
-      const float mnew = __builtin_fmaxf(ma, mb);
-      if (__any((mnew - m) * kScaleLog2 > kLazyLog2)) {
-        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * kScaleLog2);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[kb][r]), s[kb][r + 1]);
+        float ma, mb;
+        pair_values(mx, ma, mb);
+        m = __builtin_fmaxf(ma, mb);
       }
       const float mc = m * kScaleLog2;
 #pragma unroll
@@ -313,35 +312,80 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l, false);
         }
     };
+    // VALU half-step of the max-only sweep: loads of tile j+2, row max of tile j
+    auto max_phase = [&](int j) __attribute__((always_inline)) {
+      if (j + 2 < n_tiles) issue_tile(j + 2);
+      mask_tile(j);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) m_run = __builtin_fmaxf(__builtin_fmaxf(m_run, s[kb][r]), s[kb][r + 1]);
+    };
 
-    // Schedule (B_k = k-th workgroup barrier of this query tile).  Every wave runs the same
-    // sequence  MFMA(j) | barrier | softmax(j) | barrier  for j = 0 .. n-1, then the PV product
-    // of tile n-1, but waves 4-7 enter it one barrier later than waves 0-3, so between
-    // consecutive barriers one group issues MFMAs while the other is on the VALU.  Tile t is
-    // loaded into stage t % 4 at the start of softmax(t-2) -- after B_{2t-3} (group 1) or
-    // B_{2t-2} (group 2), both after the last read of tile t-4 in group 2's MFMA(t-3) -- and
-    // waited for at the end of MFMA(t-1), before the barrier B_{2t} after which group 1 reads it.
-    issue_tile(0);
-    if (n_tiles > 1) issue_tile(1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    barrier();
-    if (!first_group) barrier();
-    mfma_phase(0, yes, no);
-    barrier();
-    softmax_phase(0);
-    barrier();
-    if (n_tiles > 1) {
-      int j = 1;
-      do {
-        mfma_phase(j, yes, yes);
-        barrier();
-        softmax_phase(j);
-        barrier();
-      } while (++j < n_tiles);
+    // One sweep over all keys (kExp: softmax and PV product; else S^T and row max only).
+    // Schedule (B_k = k-th workgroup barrier of the sweep).  Every wave runs the same sequence
+    // MFMA(j) | barrier | softmax(j) | barrier  for j = 0 .. n-1, then the PV product of tile
+    // n-1, but waves 4-7 enter it one barrier later than waves 0-3, so between consecutive
+    // barriers one group issues MFMAs while the other is on the VALU.  Tile t is loaded into
+    // stage t % 4 at the start of softmax(t-2) -- after B_{2t-3} (group 1) or B_{2t-2} (group 2),
+    // both after the last read of tile t-4 in group 2's MFMA(t-3) -- and waited for at the end
+    // of MFMA(t-1), before the barrier B_{2t} after which group 1 reads it.
+    auto sweep = [&](auto exp_tag, bool set_ref) __attribute__((always_inline)) {
+      constexpr bool kExp = decltype(exp_tag)::value;
+      if constexpr (kExp) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+        l = 0.0f;
+      }
+      issue_tile(0);
+      if (n_tiles > 1) issue_tile(1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      barrier();
+      if (!first_group) barrier();
+      mfma_phase(0, yes, no);
+      barrier();
+      if constexpr (kExp) softmax_phase(0, set_ref);
+      else max_phase(0);
+      barrier();
+      if (n_tiles > 1) {
+        int j = 1;
+        do {
+          mfma_phase(j, yes, exp_tag);
+          barrier();
+          if constexpr (kExp) softmax_phase(j, false);
+          else max_phase(j);
+          barrier();
+        } while (++j < n_tiles);
+      }
+      if constexpr (kExp) mfma_phase(n_tiles, no, yes);
+      if (first_group) barrier();
+      barrier();   // every wave is done with the LDS ring before the next loads
+    };
+
+    if constexpr (!kExact) {
+      sweep(yes, true);
+      {
+        float la, lb;
+        pair_values(l, la, lb);
+        const bool over = !(la + lb <= kSumLimit);
+        if (lane == 0) redo_flag[wv] = __any(over) ? 1 : 0;
+      }
+      __syncthreads();
+      int redo = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) redo |= redo_flag[w];
+      __syncthreads();   // every wave has read the flags before they are written again
+      if (__builtin_amdgcn_readfirstlane(redo) != 0) return true;
+    } else {
+      m_run = kNeg;
+      sweep(no, false);
+      float ma, mb;
+      pair_values(m_run, ma, mb);
+      m = __builtin_fmaxf(ma, mb);
+      sweep(yes, false);
     }
-    mfma_phase(n_tiles, no, yes);
-    if (first_group) barrier();
-    barrier();   // every wave is done with the LDS ring before the next tile's loads
 
     // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row
     float la, lb;
@@ -359,6 +403,53 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
           *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
         }
     }
+  }
+  return false;
+}
+
+// The value of lane 0 (the same in every lane), as the compiler's uniform value.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <typename T>
+__device__ __forceinline__ T* uniform(T* x) {
+  const uint64_t u = reinterpret_cast<uint64_t>(x);
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)u);
+  const uint64_t hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return reinterpret_cast<T*>((hi << 32) | lo);
+}
+
+// The exact path, out of line: it runs only for query tiles whose scores outgrow the first 64
+// keys' maximum by far, and keeping its code out of the kernel body keeps the common path's
+// register allocation and schedule as they are.  Arguments of a device function arrive in
+// VGPRs; each is made uniform again, so that the buffer descriptors stay scalar.
+__device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                                          uint16_t* o, int heads, int s_q, int s_kv, int q_tiles,
+                                                          int total, int per_xcd, int n_slots, int tile) {
+  Params p;
+  p.q = uniform(q);
+  p.k = uniform(k);
+  p.v = uniform(v);
+  p.o = uniform(o);
+  p.heads = uniform(heads);
+  p.s_q = uniform(s_q);
+  p.s_kv = uniform(s_kv);
+  p.q_tiles = uniform(q_tiles);
+  p.total = uniform(total);
+  p.per_xcd = uniform(per_xcd);
+  p.n_slots = uniform(n_slots);
+  attn_tile<true>(p, uniform(tile));
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params p) {
+  // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes query tiles slot, slot +
+  // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
+  // query tiles of one head in lockstep and read each K/V tile through their shared L2.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
+    const int tile = xcd * p.per_xcd + t_local;
+    if (tile >= p.total) break;
+    if (attn_tile<false>(p, tile))
+      attn_tile_exact(p.q, p.k, p.v, p.o, p.heads, p.s_q, p.s_kv, p.q_tiles, p.total, p.per_xcd, p.n_slots, tile);
   }
 }
 
