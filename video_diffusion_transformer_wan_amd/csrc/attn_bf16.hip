@@ -102,7 +102,8 @@ __device__ __forceinline__ void pair_values(float x, float& a, float& b) {
 // Workgroup barrier without the release fence of __syncthreads(): the fence would make every
 // wave wait here for its in-flight direct-to-LDS loads (vmcnt(0)), which this kernel waits for
 // explicitly, one half-step later.  The memory clobber keeps the compiler from moving LDS reads
-// across it; no wave has an LDS read in flight at a barrier (each half-step consumes its reads).
+// across it.  LDS reads in flight at a barrier only target tiles that no load overwrites before
+// the half-step after it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // Buffer resource over [base, base + bytes); loads past the end return zeros.
@@ -111,6 +112,21 @@ __device__ __forceinline__ int clamp_bytes(int64_t bytes) {
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, clamp_bytes(bytes), (int)kRsrcFlags);
+}
+// The same descriptor as four words, for the inline-asm loads below.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const u32x4_t r = {(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, (unsigned)clamp_bytes(bytes), kRsrcFlags};
+  return r;
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at LDS address
+// lds_addr + 16 i.  Inline asm, because the compiler cannot tell the stages of the LDS ring apart
+// and would make every LDS read after such a load wait for it -- among them the reads of the
+// previous tile that the softmax half-step issues right after its loads.  The kernel waits for
+// these loads itself (s_waitcnt vmcnt) before the barrier after which any wave reads their data.
+__device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
 }
 
 // [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
@@ -130,6 +146,7 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
   const bool first_group = wv < kWaves / 2;
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  const unsigned lds_ring = (unsigned)(uintptr_t)(lds_void_t*)smem;   // LDS address of the ring
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
   const int n_tiles = (p.s_kv + kBN - 1) / kBN;
 
@@ -187,13 +204,13 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
 
     auto issue_tile = [&](int j) __attribute__((always_inline)) {
       const int64_t off = (int64_t)j * kBN * stride;
-      const __amdgpu_buffer_rsrc_t kr = make_rsrc(kbase + off, kv_bytes - off);
-      const __amdgpu_buffer_rsrc_t vr = make_rsrc(vbase + off, kv_bytes - off);
-      unsigned char* st = smem + (j % kStages) * kStageBytes + 2048 * wv;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st), 16, k_src[0], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_void_t*)(st + 1024), 16, k_src[1], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes), 16, v_src[0], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t*)(st + kKBytes + 1024), 16, v_src[1], 0, 0, 0);
+      const u32x4_t kr = rsrc_words(kbase + off, kv_bytes - off);
+      const u32x4_t vr = rsrc_words(vbase + off, kv_bytes - off);
+      const unsigned st = lds_ring + (unsigned)((j % kStages) * kStageBytes + 2048 * wv);
+      dma_b128(kr, st, k_src[0]);
+      dma_b128(kr, st + 1024, k_src[1]);
+      dma_b128(vr, st + kKBytes, v_src[0]);
+      dma_b128(vr, st + kKBytes + 1024, v_src[1]);
     };
 
     f32x16_t o[4];
@@ -202,37 +219,49 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
     f32x16_t s[2];          // S^T of the newest tile, per 32-key block
     unsigned pk[2][8];      // bf16 P^T of the tile awaiting its PV product (pairs of S^T registers)
 
-    // MFMA half-step: S^T of tile j (kQK), then the PV product of tile j-1 (kPV), as one stream
-    // of 8 steps of 4 MFMAs (4 S^T steps over 32 channels each, 4 PV steps over 16 keys each).
-    // The LDS operands of step i+1 are read while step i issues its MFMAs (two operand sets);
-    // the scheduling barriers keep that order, and the register footprint, as written.
+    // V^T operands of keys 16t .. 16t+15 of tile jj, the four 32-channel blocks
+    auto read_v = [&](int jj, int t, bf16x8_t (&f)[4]) __attribute__((always_inline)) {
+      const unsigned char* vst = smem + (jj % kStages) * kStageBytes;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const unsigned char* vp = vst + (v_rd0 ^ (64 * db)) + 4096 * t;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
+        const i16x4_t cat[2] = {lo, hi};
+        f[db] = __builtin_bit_cast(bf16x8_t, cat);
+      }
+    };
+    bf16x8_t pv_first[4];   // V^T operands of the first PV step, read ahead by the softmax half-step
+
+    // MFMA half-step: S^T of tile j (kQK) and the PV product of tile j-1 (kPV), as one stream of
+    // steps of 4 MFMAs (4 S^T steps over 32 channels each, 4 PV steps over 16 keys each).  A PV
+    // step comes first because its operands (tile j-1) may be read before the barrier that opens
+    // this half-step: the softmax half-step before it reads them, so the matrix core does not
+    // wait for LDS at the start.  The LDS operands of step i+1 are read
+    // while step i issues its MFMAs (two operand sets); the scheduling barriers keep that order,
+    // and the register footprint, as written.
     auto mfma_phase = [&](int j, auto qk_tag, auto pv_tag) __attribute__((always_inline)) {
       constexpr bool kQK = decltype(qk_tag)::value;
       constexpr bool kPV = decltype(pv_tag)::value;
       const unsigned char* ks = smem + (j % kStages) * kStageBytes;
-      const unsigned char* vst = smem + ((j + kStages - 1) % kStages) * kStageBytes;
       // raised issue priority: the SIMD's other wave is in its softmax half-step, and its VALU
       // stream would otherwise delay these MFMAs
       __builtin_amdgcn_s_setprio(3);
-      constexpr int kFirst = kQK ? 0 : 4;
-      constexpr int kSteps = kPV ? 8 : 4;
+      constexpr int kN = (kQK ? 4 : 0) + (kPV ? 4 : 0);
+      // step at position i (0-3 S^T channel steps, 4-7 PV key steps): the first PV step, then
+      // S^T (done early, so the softmax half-step after this one need not wait for it), then the
+      // remaining PV steps
+      auto step_at = [](int i) { return !kPV ? i : (!kQK ? i + 4 : (i == 0 ? 4 : (i <= 4 ? i - 1 : i))); };
       bf16x8_t ring[2][4];
-      auto read_step = [&](int i, bf16x8_t (&f)[4]) {
-        if (i < 4) {   // channels 32i .. 32i+31 (c = 2i, 2i+1) of both 32-key blocks
-          const int o0 = k_rd0 ^ (64 * i), o1 = k_rd0 ^ (64 * i + 32);
+      auto read_step = [&](int st, bf16x8_t (&f)[4]) {
+        if (st < 4) {   // channels 32st .. 32st+31 (c = 2st, 2st+1) of both 32-key blocks
+          const int o0 = k_rd0 ^ (64 * st), o1 = k_rd0 ^ (64 * st + 32);
           f[0] = *reinterpret_cast<const bf16x8_t*>(ks + o0);
           f[1] = *reinterpret_cast<const bf16x8_t*>(ks + o0 + 8192);
           f[2] = *reinterpret_cast<const bf16x8_t*>(ks + o1);
           f[3] = *reinterpret_cast<const bf16x8_t*>(ks + o1 + 8192);
-        } else {       // keys 16t .. 16t+15 of the four 32-channel blocks, t = i - 4
-#pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const unsigned char* vp = vst + (v_rd0 ^ (64 * db)) + 4096 * (i - 4);
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
-            const i16x4_t cat[2] = {lo, hi};
-            f[db] = __builtin_bit_cast(bf16x8_t, cat);
-          }
+        } else {
+          read_v(j - 1, st - 4, f);
         }
       };
       if constexpr (kQK) {
@@ -241,19 +270,25 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
       }
-      read_step(kFirst, ring[0]);
+      if constexpr (kPV) {
 #pragma unroll
-      for (int i = kFirst; i < kSteps; ++i) {
-        const int cur = (i - kFirst) & 1;
-        if (i + 1 < kSteps) read_step(i + 1, ring[cur ^ 1]);
-        if (i < 4) {
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][0], qf[2 * i], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][1], qf[2 * i], s[1], 0, 0, 0);
-          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][2], qf[2 * i + 1], s[0], 0, 0, 0);
-          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][3], qf[2 * i + 1], s[1], 0, 0, 0);
+        for (int db = 0; db < 4; ++db) ring[0][db] = pv_first[db];
+      } else {
+        read_step(step_at(0), ring[0]);
+      }
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        const int cur = i & 1;
+        const int st = step_at(i);
+        if (i + 1 < kN) read_step(step_at(i + 1), ring[cur ^ 1]);
+        if (st < 4) {
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][0], qf[2 * st], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][1], qf[2 * st], s[1], 0, 0, 0);
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][2], qf[2 * st + 1], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][3], qf[2 * st + 1], s[1], 0, 0, 0);
         } else {
           // keys 16t .. 16t+15: S^T registers 8u .. 8u+7 of key block t/2
-          const int t = i - 4, kb = t >> 1, u = t & 1;
+          const int t = st - 4, kb = t >> 1, u = t & 1;
           const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
           const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
 #pragma unroll
@@ -311,6 +346,9 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
           pk[kb][r >> 1] = pp;
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l, false);
         }
+      // operands of the next half-step's first PV step (tile j, keys 0-15): tile j stays in its
+      // stage until tile j+4 is loaded, well after that half-step
+      read_v(j, 0, pv_first);
     };
     // VALU half-step of the max-only sweep: loads of tile j+2, row max of tile j
     auto max_phase = [&](int j) __attribute__((always_inline)) {
