@@ -59,8 +59,12 @@ enum wan_attn_status {
 /*
  * Attention forward.  q, k, v, o as in the header comment; batch, heads, s_q, s_kv >= 1;
  * head_dim == 128; dtype is a wan_attn_dtype; stream is a hipStream_t or NULL.
- * bf16: needs no scratch memory.  int8_fp8: allocates about s_q*heads*batch*(head_dim+4) +
- * s_kv*heads*batch*(2*head_dim+4) bytes of scratch on `stream`, freed on `stream` after use.
+ * bf16: needs no scratch memory, except when batch*heads*ceil(s_q/256) is below half the GPU's
+ * compute units and s_kv >= 193: then each query tile's keys are split into ranges attended in
+ * parallel, and about batch*heads*ceil(s_q/256)*ranges*133 KB (ranges <= 2*CUs) of scratch is
+ * allocated on `stream` and freed on `stream` after use.  int8_fp8: allocates about
+ * s_q*heads*batch*(head_dim+4) + s_kv*heads*batch*(2*head_dim+4) bytes of scratch on `stream`,
+ * freed on `stream` after use.  WAN_ATTN_ENOMEM when a scratch allocation fails.
  */
 int wan_attn_fwd(const void* q, const void* k, const void* v, void* o,
                  int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,

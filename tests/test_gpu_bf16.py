@@ -49,26 +49,35 @@ def test_batches_and_heads(b, H, s_q, s_kv):
     assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS, (rel, mx)
 
 
-def _growing_keys(s_q, s_kv, seed, growth, q_scale_rows=0, q_scale=1.0):
+def _growing_keys(s_q, s_kv, seed, growth, damped=None, q_scale=1.0, heads=2):
     """Q, K, V ~ N(0, 1) with every key from the second 64-key block on multiplied by growth
-    (and the first q_scale_rows query rows by q_scale): scores after the first tile outgrow the
-    reference maximum the kernel takes from it."""
-    q, k, v = wan_inputs.random_qkv(1, 2, s_q, s_kv, seed, device="cuda")
+    (and the query rows `damped` by q_scale): scores after the first tile outgrow the reference
+    maximum the kernel takes from it."""
+    q, k, v = wan_inputs.random_qkv(1, heads, s_q, s_kv, seed, device="cuda")
     k = k.clone()
     k[:, 64:] = (k[:, 64:].float() * growth).to(torch.bfloat16)
-    if q_scale_rows:
+    if damped is not None:
         q = q.clone()
-        q[:, :q_scale_rows] = (q[:, :q_scale_rows].float() * q_scale).to(torch.bfloat16)
+        q[:, damped] = (q[:, damped].float() * q_scale).to(torch.bfloat16)
     return q, k, v
 
 
-@pytest.mark.parametrize("growth,q_rows", [(6.0, 0), (40.0, 0), (40.0, 100)])
-def test_scores_outgrowing_the_first_tile(growth, q_rows):
+@pytest.mark.parametrize("growth,damped,s_kv,heads,s_q", [(6.0, None, 1000, 2, 300), (40.0, None, 1000, 2, 300),
+                                                           (40.0, "first100", 1000, 2, 300),
+                                                           (40.0, "every32", 1000, 2, 300),
+                                                           (40.0, "every32", 20000, 2, 300),
+                                                           (40.0, "every32", 1000, 64, 600)])
+def test_scores_outgrowing_the_first_tile(growth, damped, s_kv, heads, s_q):
     # growth 6: later scores exceed the first tile's maximum by up to ~2^30 in P, which the fixed
     # reference absorbs; growth 40: P would overflow (row sums past 2^64), so the query tiles take
-    # the exact path (row max sweep, then softmax against it); q_rows: only some rows overflow
-    print(f"growing keys x{growth}, {q_rows} damped rows", flush=True)
-    q, k, v = _growing_keys(300, 1000, seed=91, growth=growth, q_scale_rows=q_rows, q_scale=0.02)
+    # the exact path (row max sweep, then softmax against it).  damped rows do not overflow:
+    # "first100" = rows 0-99; "every32" = rows 0, 32, 64, ..., lane 0 of every wave, so that only
+    # other lanes' rows call for the exact path.  s_kv 1000 runs with the keys split into ranges
+    # (2 heads x 2 query tiles are too few to fill the GPU), s_kv 20000 as well with longer ranges;
+    # 64 heads x 3 query tiles run unsplit.
+    print(f"growing keys x{growth}, damped {damped}, s_kv {s_kv}, heads {heads}, s_q {s_q}", flush=True)
+    rows = {None: None, "first100": np.arange(100), "every32": np.arange(0, s_q, 32)}[damped]
+    q, k, v = _growing_keys(s_q, s_kv, seed=91, growth=growth, damped=rows, q_scale=0.02, heads=heads)
     out = wan.attention(q, k, v)
     torch.cuda.synchronize()
     got = to_np(out)

@@ -196,10 +196,29 @@ int wan_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t b
   hipStream_t st = static_cast<hipStream_t>(stream);
   WAN_LOG("fwd dtype=%d b=%lld H=%lld s_q=%lld s_kv=%lld", dtype, (long long)batch,
           (long long)heads, (long long)s_q, (long long)s_kv);
-  if (dtype == WAN_ATTN_BF16) return from_hip(wan::launch_attn_bf16(q, k, v, o, sh, st), "bf16 attention launch");
+  hipMemPool_t pool;
+  if (dtype == WAN_ATTN_BF16) {
+    const int split = wan::attn_bf16_split(sh);
+    if (split == 1) return from_hip(wan::launch_attn_bf16(q, k, v, o, sh, st), "bf16 attention launch");
+    // too few query tiles to fill the GPU: key ranges in parallel, partial results in
+    // stream-ordered scratch, combined into o, scratch released on the stream
+    rc = pool_for_current_device(&pool);
+    if (rc) return rc;
+    const size_t bytes = wan::attn_bf16_split_bytes(sh, split);
+    if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) return WAN_ATTN_ENOMEM;
+    void* ws = nullptr;
+    hipError_t e = hipMallocFromPoolAsync(&ws, bytes, pool, st);
+    if (e != hipSuccess || ws == nullptr) {
+      WAN_LOG("scratch allocation of %zu bytes failed", bytes);
+      return WAN_ATTN_ENOMEM;
+    }
+    rc = from_hip(wan::launch_attn_bf16_split(q, k, v, o, sh, split, ws, st), "bf16 split attention launch");
+    hipError_t fe = hipFreeAsync(ws, st);
+    if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
+    return rc;
+  }
 
   // 8-bit: quantise into stream-ordered scratch, attend, release the scratch on the stream.
-  hipMemPool_t pool;
   rc = pool_for_current_device(&pool);
   if (rc) return rc;
   const Attn8Layout L = attn8_layout(batch, heads, s_q, s_kv);

@@ -45,6 +45,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -75,9 +77,12 @@ struct Params {
   int s_q;
   int s_kv;
   int q_tiles;
-  int total;      // q_tiles * batch * heads
-  int per_xcd;    // ceil(total / 8): query tiles handled by each XCD
+  int total;      // work items: q_tiles * batch * heads * split
+  int per_xcd;    // ceil(total / 8): work items handled by each XCD
   int n_slots;    // workgroups per XCD (gridDim.x / 8)
+  int split;      // key ranges per query tile (1: the whole key sequence)
+  int split_tiles;   // 64-key tiles per key range
+  float* ws;      // split > 1: partial results, [item][256][128] O then [item][256][2] (m, l)
 };
 
 __device__ __forceinline__ int swap23(int x) {
@@ -138,8 +143,13 @@ __shared__ int redo_flag[kWaves];
 // kExact = false: one sweep against the max of the first 64 keys; writes O and returns false,
 // or returns true (and writes nothing) when some row sum of the tile passed 2^64.
 // kExact = true: one sweep for the row maxima, one softmax sweep against them; writes O.
-template <bool kExact>
-__device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
+// kSplit: work item `item` is key range item % split of query tile item / split; instead of O it
+// writes the unnormalised O, the reference max m and the row sum l of that range to p.ws.
+template <bool kExact, bool kSplit>
+__device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
+  const int tile = kSplit ? item / p.split : item;
+  const int k0 = kSplit ? (item - tile * p.split) * p.split_tiles * kBN : 0;   // first key of the range
+  const int s_kv = kSplit ? min(p.s_kv - k0, p.split_tiles * kBN) : p.s_kv;    // keys in the range
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -148,7 +158,7 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
   const int h = lane >> 5;
   const unsigned lds_ring = (unsigned)(uintptr_t)(lds_void_t*)smem;   // LDS address of the ring
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
-  const int n_tiles = (p.s_kv + kBN - 1) / kBN;
+  const int n_tiles = (s_kv + kBN - 1) / kBN;
 
   // ---- direct global -> LDS tile loads: wave wv fills 1 KB blocks 2wv and 2wv+1 of the K tile
   // and of the V tile; lane i writes bytes 16i .. 16i+15 of its block.
@@ -184,10 +194,11 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
     const int hh = bh - bb * p.heads;
 
     const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
-    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
-    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+    const int64_t kv_head = (((int64_t)bb * p.s_kv + k0) * p.heads + hh) * kHeadDim * 2;   // first key of the range
+    const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kv_head;
+    const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kv_head;
     uint16_t* obase = p.o + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
-    const int64_t kv_bytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
+    const int64_t kv_bytes = (int64_t)(s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
 
     // ---- Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7
     // (rows past s_q read as zeros and are never stored)
@@ -308,13 +319,13 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
     // keys past the end of the sequence (last tile only) get a score that exp2 turns into 0
     auto mask_tile = [&](int j) __attribute__((always_inline)) {
       const int kv0 = j * kBN;
-      if (kv0 + kBN > p.s_kv) {
+      if (kv0 + kBN > s_kv) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = kv0 + swap23(32 * kb + 8 * (r >> 2) + 4 * h + (r & 3));
-            if (key >= p.s_kv) s[kb][r] = kNeg;
+            if (key >= s_kv) s[kb][r] = kNeg;
           }
       }
     };
@@ -408,7 +419,9 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
         float la, lb;
         pair_values(l, la, lb);
         const bool over = !(la + lb <= kSumLimit);
-        if (lane == 0) redo_flag[wv] = __any(over) ? 1 : 0;
+        // the ballot in converged code: inside the lane-0 branch it would count lane 0's row only
+        const bool wave_over = __any(over);
+        if (lane == 0) redo_flag[wv] = wave_over ? 1 : 0;
       }
       __syncthreads();
       int redo = 0;
@@ -428,8 +441,26 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int tile) {
     // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row
     float la, lb;
     pair_values(l, la, lb);
-    const float inv = 1.0f / (la + lb);
     const int row = q0 + l32;
+    if constexpr (kSplit) {   // partial result of this key range (the combining kernel divides)
+      if (row < p.s_q) {
+        const int64_t r = (int64_t)item * kBM + wv * 32 + l32;
+        float* dst = p.ws + r * kHeadDim + 4 * h;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4_t x = {o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+            *reinterpret_cast<f32x4_t*>(dst + 32 * db + 8 * g) = x;
+          }
+        if (h == 0) {
+          const f32x2_t ml = {m, la + lb};
+          *reinterpret_cast<f32x2_t*>(p.ws + (int64_t)p.total * kBM * kHeadDim + 2 * r) = ml;
+        }
+      }
+      return false;
+    }
+    const float inv = 1.0f / (la + lb);
     if (row < p.s_q) {
       uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
 #pragma unroll
@@ -459,9 +490,11 @@ __device__ __forceinline__ T* uniform(T* x) {
 // keys' maximum by far, and keeping its code out of the kernel body keeps the common path's
 // register allocation and schedule as they are.  Arguments of a device function arrive in
 // VGPRs; each is made uniform again, so that the buffer descriptors stay scalar.
+template <bool kSplit>
 __device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                           uint16_t* o, int heads, int s_q, int s_kv, int q_tiles,
-                                                          int total, int per_xcd, int n_slots, int tile) {
+                                                          int total, int split, int split_tiles, float* ws,
+                                                          int item) {
   Params p;
   p.q = uniform(q);
   p.k = uniform(k);
@@ -472,41 +505,72 @@ __device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, con
   p.s_kv = uniform(s_kv);
   p.q_tiles = uniform(q_tiles);
   p.total = uniform(total);
-  p.per_xcd = uniform(per_xcd);
-  p.n_slots = uniform(n_slots);
-  attn_tile<true>(p, uniform(tile));
+  p.per_xcd = 0;
+  p.n_slots = 0;
+  p.split = uniform(split);
+  p.split_tiles = uniform(split_tiles);
+  p.ws = uniform(ws);
+  attn_tile<true, kSplit>(p, uniform(item));
 }
 
+template <bool kSplit>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params p) {
-  // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes query tiles slot, slot +
+  // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes work items slot, slot +
   // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
   // query tiles of one head in lockstep and read each K/V tile through their shared L2.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
-    const int tile = xcd * p.per_xcd + t_local;
-    if (tile >= p.total) break;
-    if (attn_tile<false>(p, tile))
-      attn_tile_exact(p.q, p.k, p.v, p.o, p.heads, p.s_q, p.s_kv, p.q_tiles, p.total, p.per_xcd, p.n_slots, tile);
+    const int item = xcd * p.per_xcd + t_local;
+    if (item >= p.total) break;
+    if (attn_tile<false, kSplit>(p, item))
+      attn_tile_exact<kSplit>(p.q, p.k, p.v, p.o, p.heads, p.s_q, p.s_kv, p.q_tiles, p.total, p.split,
+                              p.split_tiles, p.ws, item);
   }
 }
 
-}  // namespace
+// Combines the key ranges of a split run: for one query row (one wave, two channels per lane),
+// O = sum_s w_s O_s / sum_s w_s l_s with w_s = 2^((m_s - max_s m_s) log2(e)/sqrt(128)), the
+// ranges' partial sums brought to a common reference max.  Lane s holds range s's (m, l) (at
+// most 64 ranges), so max and sum are wave reductions; the O loads are unrolled to overlap.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x = __builtin_fmaxf(x, __shfl_xor(x, d));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+  return x;
+}
+__global__ __launch_bounds__(256) void attn_bf16_combine_kernel(const Params p) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (b*H + h) * s_q + i
+  const int lane = threadIdx.x & 63;
+  const int64_t rows = (int64_t)(p.total / p.split) / p.q_tiles * p.s_q;   // b*H*s_q
+  if (row >= rows) return;
+  const int64_t bh = row / p.s_q;
+  const int i = (int)(row - bh * p.s_q);
+  const int64_t first = (bh * p.q_tiles + i / kBM) * p.split * kBM + i % kBM;   // range 0's row
+  const float* ml = p.ws + (int64_t)p.total * kBM * kHeadDim;
+  f32x2_t mine = {kNeg, 0.0f};
+  if (lane < p.split) mine = *reinterpret_cast<const f32x2_t*>(ml + 2 * (first + (int64_t)lane * kBM));
+  const float mx = wave_max(mine[0]);
+  const float w = lane < p.split ? __builtin_amdgcn_exp2f((mine[0] - mx) * kScaleLog2) : 0.0f;
+  const float inv = 1.0f / wave_sum(w * mine[1]);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll 8
+  for (int sp = 0; sp < p.split; ++sp) {
+    const float ws = __shfl(w, sp);
+    const f32x2_t x = *reinterpret_cast<const f32x2_t*>(p.ws + (first + (int64_t)sp * kBM) * kHeadDim + 2 * lane);
+    a0 += ws * x[0];
+    a1 += ws * x[1];
+  }
+  const int64_t bb = bh / p.heads, hh = bh - bb * p.heads;
+  *reinterpret_cast<unsigned*>(p.o + ((bb * p.s_q + i) * p.heads + hh) * kHeadDim + 2 * lane) =
+      cvt_pk_bf16(a0 * inv, a1 * inv);
+}
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
-                            const AttnShape& sh, hipStream_t stream) {
-  Params p;
-  p.q = static_cast<const uint16_t*>(q);
-  p.k = static_cast<const uint16_t*>(k);
-  p.v = static_cast<const uint16_t*>(v);
-  p.o = static_cast<uint16_t*>(o);
-  p.heads = (int)sh.heads;
-  p.s_q = (int)sh.s_q;
-  p.s_kv = (int)sh.s_kv;
-  p.q_tiles = (int)ceil_div(sh.s_q, kBM);
-  p.total = (int)(p.q_tiles * sh.batch * sh.heads);
-  p.per_xcd = (int)ceil_div(p.total, 8);
-  // one workgroup per CU (the LDS ring and the registers allow no second one)
+int device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0, n = 0;
@@ -516,9 +580,68 @@ hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o
     else
       cus = 256;
   }
+  return cus;
+}
+
+Params make_params(const void* q, const void* k, const void* v, void* o, const AttnShape& sh, int split,
+                   void* ws) {
+  Params p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<uint16_t*>(o);
+  p.heads = (int)sh.heads;
+  p.s_q = (int)sh.s_q;
+  p.s_kv = (int)sh.s_kv;
+  p.q_tiles = (int)ceil_div(sh.s_q, kBM);
+  const int n_kt = (int)ceil_div(sh.s_kv, kBN);
+  p.split = split;
+  p.split_tiles = (int)ceil_div(n_kt, split);
+  p.ws = static_cast<float*>(ws);
+  p.total = (int)(p.q_tiles * sh.batch * sh.heads * split);
+  p.per_xcd = (int)ceil_div(p.total, 8);
+  // one workgroup per CU (the LDS ring and the registers allow no second one)
+  const int cus = device_cus();
   p.n_slots = (int)(p.per_xcd < cus / 8 ? p.per_xcd : cus / 8);
-  const dim3 grid((unsigned)(8 * p.n_slots));
-  hipLaunchKernelGGL(attn_fwd_bf16_kernel, grid, dim3(kThreads), 0, stream, p);
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
+                            const AttnShape& sh, hipStream_t stream) {
+  const Params p = make_params(q, k, v, o, sh, 1, nullptr);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)(8 * p.n_slots)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+int attn_bf16_split(const AttnShape& sh) {
+  // Too few query tiles to fill the chip: split each tile's keys into ranges of >= 2 tiles, aiming
+  // at about two work items per CU.
+  const int64_t tiles = ceil_div(sh.s_q, kBM) * sh.batch * sh.heads;
+  const int64_t n_kt = ceil_div(sh.s_kv, kBN);
+  const int64_t cus = device_cus();
+  if (2 * tiles > cus || n_kt < 4) return 1;
+  int64_t split = ceil_div(2 * cus, tiles);
+  if (split > n_kt / 2) split = n_kt / 2;
+  if (split > 64) split = 64;   // one wave combines all ranges of a row
+  if (split < 2) return 1;
+  return (int)ceil_div(n_kt, ceil_div(n_kt, split));   // no empty range
+}
+
+size_t attn_bf16_split_bytes(const AttnShape& sh, int split) {
+  const int64_t items = ceil_div(sh.s_q, kBM) * sh.batch * sh.heads * split;
+  return (size_t)items * kBM * (kHeadDim + 2) * sizeof(float);
+}
+
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o,
+                                  const AttnShape& sh, int split, void* ws, hipStream_t stream) {
+  const Params p = make_params(q, k, v, o, sh, split, ws);
+  hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)(8 * p.n_slots)), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = sh.batch * sh.heads * sh.s_q;
+  hipLaunchKernelGGL(attn_bf16_combine_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -16,6 +16,13 @@ struct AttnShape {
 // bf16 flash-attention forward: q, k, v, o bf16 [b, s, H, 128].
 hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
                             const AttnShape& sh, hipStream_t stream);
+// Key ranges per query tile for shapes with too few query tiles to fill the chip (1: none),
+// the scratch bytes that split needs, and the split launch (attention over key ranges, then the
+// combination of the ranges into o).
+int attn_bf16_split(const AttnShape& sh);
+size_t attn_bf16_split_bytes(const AttnShape& sh, int split);
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o,
+                                  const AttnShape& sh, int split, void* ws, hipStream_t stream);
 
 // 8-bit path, stage 1: per-channel maxima into `chan_max` ([b, H, 3, 128] f32), then codes and
 // scales (layouts documented in include/wan_attn.h).
