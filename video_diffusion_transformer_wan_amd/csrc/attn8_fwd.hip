@@ -296,7 +296,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
           const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[kb][r + 2], f, bias));
           const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[kb][r + 3], f, bias));
           l += (p0 + p1) + (p2 + p3);
-          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+          // both halves of the word are written, so the old value passed in is never kept (a
+          // constant there would cost a v_mov per word)
+          int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (int)pb[4 * kb + wd], false);
           x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
           pb[4 * kb + wd] = (unsigned)x;
         }

@@ -28,8 +28,9 @@
 //    the only risk is that a later, much larger score overflows P; then the row sum exceeds
 //    2^64 (or is infinite), and the query tile is swept again -- once for the true row max
 //    (S^T only), once for the result.  The loop carries no running max, no vote and no
-//    rescaling of O.  Row sums come from the bf16-rounded P through v_dot2 so numerator and
-//    denominator see the same weights.
+//    rescaling of O.  Row sums add the fp32 P with v_add_f32: v_dot2_f32_bf16 on the packed P
+//    would issue to the matrix-core pipe, where it waits behind the other wave's MFMAs (about
+//    160 cycles each, against 6 on an idle pipe).
 //  * Workgroups are numbered so that the 32 CUs of one XCD work on consecutive query tiles of the
 //    same head and share its K/V stream in their L2.
 
@@ -186,7 +187,6 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
     const int x = 2 * (g & 1) + (q >> 1);
     v_rd0 = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * kq + 16 * x + 8 * (q & 1);
   }
-  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   {
     const int qt = tile % p.q_tiles;
     const int bh = tile / p.q_tiles;
@@ -355,7 +355,7 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], kScaleLog2, -mc));
           const unsigned pp = cvt_pk_bf16(p0, p1);
           pk[kb][r >> 1] = pp;
-          l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, l, false);
+          l += p0 + p1;
         }
       // operands of the next half-step's first PV step (tile j, keys 0-15): tile j stays in its
       // stage until tile j+4 is loaded, well after that half-step
