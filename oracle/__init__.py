@@ -20,6 +20,9 @@ Modules:
   exact     -- exact attention in float64, two passes (global row max, then exp / sum / weighted V).
   numerics  -- bit-level rounding to bfloat16, OCP FP8 E4M3 ("e4m3fn") and int8 codes.
   attn8     -- the 8-bit scheme, step by step, as a diagnostic reference for the 8-bit GPU path.
+  backward  -- the exact gradients dQ, dK, dV (chain rule through the row softmax) and the row
+               log-sum-exp, in float64: the attention backward (beta = 8 term of the cost model,
+               same explainer, section "先看现象").
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py``.  The product path (the HIP library and its Python binding) never imports, links or
@@ -36,3 +39,4 @@ from .numerics import (  # noqa: F401
     int8_codes,
 )
 from .attn8 import attn8_emulate, attn8_quantize  # noqa: F401
+from .backward import attention_backward, lse_rows, dq_rows  # noqa: F401
