@@ -6,7 +6,9 @@ One step = one call of the C ABI's wan_attn_fwd on the workload's full shape, in
 HBM.  Prints ONE JSON line: the headline is the bf16 self-attention of the Wan-14B-shaped 720p,
 81-frame sequence (b=2 for cond/uncond, 40 heads, 75,600 tokens, head_dim 128), in TFLOP/s
 counted as 4*b*heads*s_q*s_kv*head_dim; "configs" adds every other workload (480p frame,
-Wan-1.3B 480p, text cross-attention, the 8-bit path at the 720p shape) measured the same way.
+Wan-1.3B 480p, text cross-attention, the 8-bit path at the 720p shape) measured the same way, and
+the bf16 attention backward (dQ, dK, dV from the forward's output and row log-sum-exp) at the
+Wan-1.3B 480p and Wan-14B 720p shapes, in TFLOP/s counted as 8*b*heads*s_q*s_kv*head_dim.
 "roofline" is for the dominant kernel, "cpu_baseline" times the plain fp64 CPU oracle on a
 bounded sample of query rows of the same workload.
 """
@@ -137,6 +139,28 @@ def run_workload(name, steps, warmup):
     return w, (q, k, v), res, kernel_ms
 
 
+def run_backward(name, steps, warmup):
+    """The bf16 backward at a workload's shape: one step = one wan_attn_bwd call (the forward that
+    produces o and lse runs once, before the timed region)."""
+    import torch
+    import video_diffusion_transformer_wan_amd as wan
+    import wan_inputs
+    w = wan_inputs.WORKLOADS[name]
+    q, k, v = wan_inputs.make_qkv(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
+    d_o = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o, lse = wan.attention_with_lse(q, k, v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    fn = lambda: wan.wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, w.batch, w.heads, w.s_q, w.s_kv,
+                                  w.head_dim, stream)
+    ms = time_calls(fn, steps, warmup, stream)
+    flops = 2.0 * w.flops   # the pages' beta = 8 against the forward's 4
+    return {"workload": name, "path": "bf16 backward", "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12,
+            "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+            "mfma_tflops": 3.5 * w.flops / (ms * 1e-3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +169,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--backward-only", default=None, metavar="WORKLOAD",
+                    help="only time the bf16 backward at this workload's shape (for profiling)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -162,6 +188,10 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "dispatches": max(1, args.steps)}), flush=True)
+        return
+    if args.backward_only:
+        res = run_backward(args.backward_only, args.steps, args.warmup)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}), flush=True)
         return
     import video_diffusion_transformer_wan_amd as wan
     import wan_inputs
@@ -196,6 +226,14 @@ def main():
             except Exception as e:  # report, do not hide the headline
                 res = {"workload": name, "error": str(e)}
             configs[name] = res
+            torch.cuda.empty_cache()
+        for name in ("wan1.3b_480p81f_self", HEADLINE):
+            try:
+                small = wan_inputs.WORKLOADS[name].flops < 1e13
+                res = run_backward(name, max(2, args.steps // 2) * (5 if small else 1), 1)
+            except Exception as e:
+                res = {"workload": name, "error": str(e)}
+            configs[name + ":backward"] = res
             torch.cuda.empty_cache()
 
     line = {

@@ -12,7 +12,8 @@
  * Layouts (all entry points): row-major, dense, contiguous, device memory
  *   q, o : [batch, s_q,  heads, head_dim]  bfloat16
  *   k, v : [batch, s_kv, heads, head_dim]  bfloat16
- * head_dim must be 128.  Pointers must be 16-byte aligned.  o must not overlap q, k or v.
+ * head_dim must be 128; heads <= 65536.  Pointers must be 16-byte aligned.  o must not overlap
+ * q, k or v.
  *
  * Ownership: the caller owns every buffer it passes; the library never frees or retains them.
  * Streams: every call only enqueues work on `stream` (a hipStream_t; NULL is the default stream)
@@ -106,6 +107,37 @@ int wan_attn8_fwd_quantized(const void* q_codes, const void* q_scale,
                             const void* v_codes, const void* v_scale, void* o,
                             int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
                             int64_t head_dim, void* stream);
+
+/*
+ * bf16 attention forward that also writes the row statistic the backward needs:
+ *   lse [batch, heads, s_q] f32 (device memory, 16-byte aligned, owned by the caller),
+ *   lse[b, h, i] = log( sum_j exp( Q[b,i,h,:] . K[b,j,h,:] / sqrt(128) ) )   (natural log).
+ * Otherwise exactly wan_attn_fwd with dtype WAN_ATTN_BF16 (same o, same scratch rules); lse must
+ * not overlap q, k, v or o.
+ */
+int wan_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, void* lse,
+                     int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                     int64_t head_dim, void* stream);
+
+/*
+ * bf16 attention backward: the gradients of the forward above with respect to q, k and v, given
+ * the upstream gradient d_o -- the beta = 8 term of the DiT cost model, the part of training that
+ * attention dominates ("Wan 2.1: VBench 86.22% ..." explainer, section "先看现象").  With
+ * S = Q K^T/sqrt(128), P = exp(S - lse) (row softmax), D_i = sum_c dO[i,c] O[i,c]:
+ *   dV = P^T dO,   dS = P * (dO V^T - D),   dQ = dS K / sqrt(128),   dK = dS^T Q / sqrt(128)
+ * per (batch, head), products in bf16 on the MFMA with fp32 accumulation, P and dS rounded to
+ * bf16 for the products, outputs rounded to bf16.
+ * Inputs: q, k, v as for the forward; o [batch, s_q, heads, 128] bf16 and lse [batch, heads, s_q]
+ * f32 from wan_attn_fwd_lse on the same q, k, v; d_o with o's layout.
+ * Outputs: dq with q's layout, dk and dv with k's layout, bf16, owned by the caller; none may
+ * overlap another output or an input.
+ * Scratch: 8 * batch * heads * ceil(s_q/64)*64 bytes allocated on `stream` and freed on `stream`
+ * after use (WAN_ATTN_ENOMEM if that fails).
+ */
+int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                 const void* lse, void* dq, void* dk, void* dv,
+                 int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim,
+                 void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* wan_attn_strerror(int code);

@@ -37,6 +37,13 @@ BF16_REL_L2 = 1e-2
 BF16_MAX_ABS = 3e-2
 INT8_REL_L2 = 6e-2
 INT8_COS = 0.995
+# Bounds of the bf16 backward's dQ, dK, dV against the exact gradients (per tensor): rel-L2, and
+# max-abs as a fraction of the largest exact magnitude.  The final rounding to bf16 alone gives a
+# relative RMS error of about 2^-7/sqrt(12) = 2.3e-3 and a worst case of 2^-8 = 0.4% at the largest
+# element; P and dS rounded to bf16 before their products add errors of the same size that average
+# out over the sums.  The bounds leave a factor of about 4 and 5 above that.
+BWD_REL_L2 = 1e-2
+BWD_MAX_REL = 2e-2
 
 
 def gather_rows(out, rows):

@@ -90,3 +90,43 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(wan, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         wan.lib()
+
+
+def _bwd(**kw):
+    """wan_attn_bwd with distinct, far-apart fake device addresses (never dereferenced: every case
+    below fails a check before the first HIP call)."""
+    lib = ensure_built()
+    names = ["q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv"]
+    args = {n: 4096 * (i + 1) for i, n in enumerate(names)}
+    args.update(b=1, H=1, sq=1, skv=1, d=128)
+    args.update(kw)
+    return lib.wan_attn_bwd(*[args[n] for n in names], args["b"], args["H"], args["sq"], args["skv"],
+                            args["d"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), wan.WAN_ATTN_EINVAL),
+    (dict(lse=None), wan.WAN_ATTN_EINVAL),
+    (dict(dv=None), wan.WAN_ATTN_EINVAL),
+    (dict(d_o=4096 * 5 + 8), wan.WAN_ATTN_EALIGN),
+    (dict(lse=4096 * 6 + 4), wan.WAN_ATTN_EALIGN),
+    (dict(d=64), wan.WAN_ATTN_EUNSUPPORTED),
+    (dict(skv=0), wan.WAN_ATTN_EINVAL),
+    (dict(H=65537), wan.WAN_ATTN_EINVAL),         # a tile's 64 rows beyond a 32-bit byte offset
+    (dict(dq=4096 * 1), wan.WAN_ATTN_EINVAL),     # dq overlaps q
+    (dict(dk=4096 * 6), wan.WAN_ATTN_EINVAL),     # dk overlaps lse
+    (dict(dv=4096 * 8), wan.WAN_ATTN_EINVAL),     # dv overlaps dk
+])
+def test_backward_argument_checks(kw, code):
+    assert _bwd(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((16, 32, 48, 4096, None), wan.WAN_ATTN_EINVAL),
+    ((16, 32, 48, 4096, 8196), wan.WAN_ATTN_EALIGN),
+    ((16, 32, 48, 4096, 4096), wan.WAN_ATTN_EINVAL),   # lse overlaps o
+])
+def test_forward_lse_argument_checks(args, code):
+    lib = ensure_built()
+    assert lib.wan_attn_fwd_lse(*args, 1, 1, 1, 1, 128, None) == code
+    assert lib.wan_attn_fwd_lse(16, 32, 48, 4096, 8192, 1, 1, 1, 1, 96, None) == wan.WAN_ATTN_EUNSUPPORTED

@@ -1,0 +1,116 @@
+"""Parity of the bf16 attention backward (through the C ABI) with the fp64 oracle, on the GPU.
+
+The forward that feeds it (wan_attn_fwd_lse) is checked first: its row log-sum-exp against the
+oracle's, its output against wan_attn_fwd's (bit for bit).  Gradients: small and ragged shapes
+compare every element of dQ, dK and dV with the oracle's exact gradients; a Wan-sized shape
+compares sampled dQ rows with the oracle and checks dK and dV through identities that hold at any
+size (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+Bounds, per tensor over all checked elements: rel-L2 <= BWD_REL_L2 and max-abs <= BWD_MAX_REL times
+the largest magnitude of the exact gradient.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import video_diffusion_transformer_wan_amd as wan
+import wan_inputs
+from _util import BWD_MAX_REL, BWD_REL_L2, ensure_built, metrics, to_np
+
+pytestmark = pytest.mark.gpu
+
+LSE_MAX_ABS = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    ensure_built()
+    assert torch.cuda.is_available()
+
+
+def _inputs(b, H, s_q, s_kv, seed):
+    q, k, v = wan_inputs.random_qkv(b, H, s_q, s_kv, seed, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(seed + 7)
+    d_o = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    return q, k, v, d_o
+
+
+def _check_grad(name, got, ref):
+    """rel-L2 and scaled max-abs; an exact gradient that is zero (one key: softmax is constant)
+    is checked against the floor 1e-2 of the scale (inputs are N(0, 1))."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    scale = max(float(np.max(np.abs(ref))), 1e-2)
+    mx = float(np.max(np.abs(got - ref)))
+    if np.linalg.norm(ref) > 1e-12:
+        rel, _, _ = metrics(got, ref)
+    else:
+        rel = 0.0
+    print(f"  {name}: rel-L2 {rel:.2e}  max-abs {mx:.2e} (scale {scale:.2e})", flush=True)
+    assert rel <= BWD_REL_L2 and mx <= BWD_MAX_REL * scale, (name, rel, mx, scale)
+
+
+def _full_case(b, H, s_q, s_kv, seed):
+    print(f"backward b={b} H={H} s_q={s_q} s_kv={s_kv}", flush=True)
+    q, k, v, d_o = _inputs(b, H, s_q, s_kv, seed)
+    o, lse = wan.attention_with_lse(q, k, v)
+    dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
+    torch.cuda.synchronize()
+    rq, rk, rv, rlse = oracle.attention_backward(to_np(q), to_np(k), to_np(v), to_np(d_o))
+    assert np.max(np.abs(to_np(lse) - rlse)) <= LSE_MAX_ABS
+    _check_grad("dq", to_np(dq), rq)
+    _check_grad("dk", to_np(dk), rk)
+    _check_grad("dv", to_np(dv), rv)
+
+
+@pytest.mark.parametrize("b,H,s_q,s_kv", [(1, 2, 600, 4000), (2, 3, 513, 700), (1, 40, 300, 512)])
+def test_forward_lse(b, H, s_q, s_kv):
+    # (1, 2, 600, 4000) runs the split key-range path, the others the one-pass kernel
+    q, k, v, _ = _inputs(b, H, s_q, s_kv, 5)
+    o, lse = wan.attention_with_lse(q, k, v)
+    o_plain = wan.attention(q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain)
+    rows = np.array([[bb, hh, i] for bb in range(b) for hh in range(H) for i in range(s_q)])
+    ref = oracle.lse_rows(to_np(q), to_np(k), rows)
+    got = to_np(lse).reshape(-1)
+    assert np.max(np.abs(got - ref)) <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("s_q,s_kv", [(1, 1), (1, 200), (64, 64), (65, 63), (127, 129), (129, 127), (300, 1),
+                                      (200, 300), (256, 256)])
+def test_backward_ragged(s_q, s_kv):
+    _full_case(1, 2, s_q, s_kv, seed=3000 + 7 * s_q + s_kv)
+
+
+@pytest.mark.parametrize("b,H,s_q,s_kv", [(2, 3, 300, 500), (1, 4, 1000, 1000), (1, 2, 2000, 150)])
+def test_backward_batches_heads(b, H, s_q, s_kv):
+    _full_case(b, H, s_q, s_kv, seed=b * 1000 + H * 100 + s_q)
+
+
+def test_backward_wan_sized():
+    # Wan2.1-1.3B at 480p, 81 frames: 12 heads x 32,760 tokens, one batch
+    b, H, s = 1, 12, 32760
+    print(f"backward b={b} H={H} s={s}", flush=True)
+    q, k, v, d_o = _inputs(b, H, s, s, 77)
+    o, lse = wan.attention_with_lse(q, k, v)
+    dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(78)
+    rows = np.stack([np.zeros(48, np.int64), rng.integers(0, H, 48), rng.integers(0, s, 48)], 1)
+    rows[0] = [0, 0, 0]
+    rows[1] = [0, H - 1, s - 1]
+    qn, kn, vn, gn = to_np(q), to_np(k), to_np(v), to_np(d_o)
+    ref = oracle.dq_rows(qn, kn, vn, gn, rows)
+    got = to_np(dq[0, rows[:, 2], rows[:, 1], :])
+    _check_grad("dq rows", got, ref)
+    # identities: sum over keys of dK is zero; sum over keys of dV is the sum over queries of dO
+    dk64 = dk.double().sum(dim=1)
+    scale = dk.double().abs().sum(dim=1)
+    assert float((dk64.abs() / scale).max()) < 2e-2
+    sum_dv = dv.double().sum(dim=1)
+    sum_do = d_o.double().sum(dim=1)
+    rel = float((sum_dv - sum_do).norm() / sum_do.norm())
+    print(f"  sum dK / sum |dK| max {float((dk64.abs() / scale).max()):.2e}, sum dV vs sum dO rel {rel:.2e}")
+    assert rel < 1e-2

@@ -47,6 +47,8 @@ _SIGNATURES = {
     "wan_attn8_quantize_scratch_bytes": (ctypes.c_size_t, [_I64, _I64]),
     "wan_attn8_fwd_quantized": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P,
                                                _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_fwd_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_attn_version": (ctypes.c_int, []),
 }
@@ -103,6 +105,18 @@ def wan_attn_fwd(q, k, v, o, batch, heads, s_q, s_kv, head_dim, dtype, stream=No
     rc = lib().wan_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, s_q, s_kv, head_dim,
                             dtype, _stream(stream))
     _check(rc, "wan_attn_fwd")
+
+
+def wan_attn_fwd_lse(q, k, v, o, lse, batch, heads, s_q, s_kv, head_dim, stream=None):
+    rc = lib().wan_attn_fwd_lse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), batch, heads, s_q, s_kv,
+                                head_dim, _stream(stream))
+    _check(rc, "wan_attn_fwd_lse")
+
+
+def wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, s_q, s_kv, head_dim, stream=None):
+    rc = lib().wan_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+                            _ptr(dv), batch, heads, s_q, s_kv, head_dim, _stream(stream))
+    _check(rc, "wan_attn_bwd")
 
 
 def wan_attn8_quantize_scratch_bytes(batch, heads):
@@ -180,3 +194,29 @@ def attention8_from_quantized(z, b, H, s_q, s_kv, out=None, stream=None):
     wan_attn8_fwd_quantized(z["q_codes"], z["q_scale"], z["k_codes"], z["k_scale"], z["v_codes"],
                             z["v_scale"], out, b, H, s_q, s_kv, HEAD_DIM, stream)
     return out
+
+
+def attention_with_lse(q, k, v, stream=None):
+    """bf16 forward that also returns the row log-sum-exp: (o [b, s_q, H, 128] bf16,
+    lse [b, H, s_q] float32)."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    out = torch.empty_like(q)
+    lse = torch.empty((b, H, s_q), dtype=torch.float32, device=q.device)
+    wan_attn_fwd_lse(q, k, v, out, lse, b, H, s_q, s_kv, d, stream)
+    return out, lse
+
+
+def attention_backward(q, k, v, o, lse, d_o, stream=None):
+    """Gradients (dq, dk, dv) of the bf16 attention for upstream gradient d_o, from the forward's
+    output o and row log-sum-exp lse (attention_with_lse); new bfloat16 tensors."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    for name, t, shape in (("o", o, q.shape), ("d_o", d_o, q.shape)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.shape != shape:
+            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor shaped like q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (b, H, s_q):
+        raise ValueError("lse must be a contiguous float32 tensor [b, H, s_q]")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, b, H, s_q, s_kv, d, stream)
+    return dq, dk, dv

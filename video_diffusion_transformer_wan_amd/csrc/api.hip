@@ -41,8 +41,8 @@ int check_shape(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t
   if (batch < 1 || heads < 1 || s_q < 1 || s_kv < 1 || head_dim < 1) return WAN_ATTN_EINVAL;
   if (head_dim != wan::kHeadDim) return WAN_ATTN_EUNSUPPORTED;
   const int64_t kMax32 = 0x7fffffffLL;
-  if (batch > kMax32 || heads > kMax32 || s_q > kMax32 - 256 || s_kv > kMax32 - 256)
-    return WAN_ATTN_EINVAL;
+  if (batch > kMax32 || heads > 65536 || s_q > kMax32 - 256 || s_kv > kMax32 - 256)
+    return WAN_ATTN_EINVAL;   // heads: 64 token rows of one tile stay within a 32-bit byte offset
   // workgroup count (256-row query tiles) must fit in int; element counts in 2^60
   const long double tiles = (long double)wan::ceil_div(s_q, 64) * (long double)batch * heads;
   if (tiles > (long double)kMax32 - 8) return WAN_ATTN_EINVAL;
@@ -97,6 +97,41 @@ struct Attn8Layout {
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Stream-ordered scratch from the device's pool (nullptr on failure; the test hook
+// WAN_ATTN_TEST_FAIL_ALLOC makes every allocation fail).
+void* scratch_alloc(size_t bytes, hipStream_t st, int* rc) {
+  hipMemPool_t pool;
+  *rc = pool_for_current_device(&pool);
+  if (*rc) return nullptr;
+  if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) {
+    *rc = WAN_ATTN_ENOMEM;
+    return nullptr;
+  }
+  void* ws = nullptr;
+  hipError_t e = hipMallocFromPoolAsync(&ws, bytes, pool, st);
+  if (e != hipSuccess || ws == nullptr) {
+    WAN_LOG("scratch allocation of %zu bytes failed", bytes);
+    *rc = WAN_ATTN_ENOMEM;
+    return nullptr;
+  }
+  return ws;
+}
+
+// bf16 forward (lse optional).  Too few query tiles to fill the GPU: key ranges in parallel,
+// partial results in stream-ordered scratch, combined into o, scratch released on the stream.
+int fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, const wan::AttnShape& sh,
+             hipStream_t st) {
+  const int split = wan::attn_bf16_split(sh);
+  if (split == 1) return from_hip(wan::launch_attn_bf16(q, k, v, o, lse, sh, st), "bf16 attention launch");
+  int rc = WAN_ATTN_OK;
+  void* ws = scratch_alloc(wan::attn_bf16_split_bytes(sh, split), st, &rc);
+  if (!ws) return rc;
+  rc = from_hip(wan::launch_attn_bf16_split(q, k, v, o, lse, sh, split, ws, st), "bf16 split attention launch");
+  hipError_t fe = hipFreeAsync(ws, st);
+  if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
+  return rc;
+}
 
 Attn8Layout attn8_layout(int64_t b, int64_t H, int64_t s_q, int64_t s_kv) {
   Attn8Layout L;
@@ -196,39 +231,12 @@ int wan_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t b
   hipStream_t st = static_cast<hipStream_t>(stream);
   WAN_LOG("fwd dtype=%d b=%lld H=%lld s_q=%lld s_kv=%lld", dtype, (long long)batch,
           (long long)heads, (long long)s_q, (long long)s_kv);
-  hipMemPool_t pool;
-  if (dtype == WAN_ATTN_BF16) {
-    const int split = wan::attn_bf16_split(sh);
-    if (split == 1) return from_hip(wan::launch_attn_bf16(q, k, v, o, sh, st), "bf16 attention launch");
-    // too few query tiles to fill the GPU: key ranges in parallel, partial results in
-    // stream-ordered scratch, combined into o, scratch released on the stream
-    rc = pool_for_current_device(&pool);
-    if (rc) return rc;
-    const size_t bytes = wan::attn_bf16_split_bytes(sh, split);
-    if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) return WAN_ATTN_ENOMEM;
-    void* ws = nullptr;
-    hipError_t e = hipMallocFromPoolAsync(&ws, bytes, pool, st);
-    if (e != hipSuccess || ws == nullptr) {
-      WAN_LOG("scratch allocation of %zu bytes failed", bytes);
-      return WAN_ATTN_ENOMEM;
-    }
-    rc = from_hip(wan::launch_attn_bf16_split(q, k, v, o, sh, split, ws, st), "bf16 split attention launch");
-    hipError_t fe = hipFreeAsync(ws, st);
-    if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
-    return rc;
-  }
+  if (dtype == WAN_ATTN_BF16) return fwd_bf16(q, k, v, o, nullptr, sh, st);
 
   // 8-bit: quantise into stream-ordered scratch, attend, release the scratch on the stream.
-  rc = pool_for_current_device(&pool);
-  if (rc) return rc;
   const Attn8Layout L = attn8_layout(batch, heads, s_q, s_kv);
-  if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) return WAN_ATTN_ENOMEM;
-  void* ws = nullptr;
-  hipError_t e = hipMallocFromPoolAsync(&ws, L.total, pool, st);
-  if (e != hipSuccess || ws == nullptr) {
-    WAN_LOG("scratch allocation of %zu bytes failed", L.total);
-    return WAN_ATTN_ENOMEM;
-  }
+  void* ws = scratch_alloc(L.total, st, &rc);
+  if (!ws) return rc;
   unsigned char* base = static_cast<unsigned char*>(ws);
   int8_t* qc = reinterpret_cast<int8_t*>(base + L.q_codes);
   int8_t* kc = reinterpret_cast<int8_t*>(base + L.k_codes);
@@ -243,6 +251,61 @@ int wan_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t b
   if (!rc)
     rc = from_hip(wan::launch_attn8_fwd(qc, qs, kc, kscale, vc, vscale, o, sh, st),
                   "8-bit attention launch");
+  hipError_t fe = hipFreeAsync(ws, st);
+  if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
+  return rc;
+}
+
+int wan_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, void* lse, int64_t batch,
+                     int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  rc = check_qkvo(q, k, v, o, batch, heads, s_q, s_kv);
+  if (rc) return rc;
+  if (!lse) return WAN_ATTN_EINVAL;
+  if (!aligned16(lse)) return WAN_ATTN_EALIGN;
+  const int64_t lb = batch * heads * s_q * 4;
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
+  const int64_t kb = batch * s_kv * heads * wan::kHeadDim * 2;
+  if (overlaps(lse, lb, q, qb) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) || overlaps(lse, lb, o, qb))
+    return WAN_ATTN_EINVAL;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  WAN_LOG("fwd_lse b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads, (long long)s_q,
+          (long long)s_kv);
+  return fwd_bf16(q, k, v, o, static_cast<float*>(lse), sh, static_cast<hipStream_t>(stream));
+}
+
+int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                 const void* lse, void* dq, void* dk, void* dv, int64_t batch, int64_t heads,
+                 int64_t s_q, int64_t s_kv, int64_t head_dim, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  const void* ptrs[] = {q, k, v, o, d_o, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!p) return WAN_ATTN_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
+  const int64_t kb = batch * s_kv * heads * wan::kHeadDim * 2;
+  const int64_t lb = batch * heads * s_q * 4;
+  const void* ins[] = {q, k, v, o, d_o, lse};
+  const int64_t in_bytes[] = {qb, kb, kb, qb, qb, lb};
+  void* outs[] = {dq, dk, dv};
+  const int64_t out_bytes[] = {qb, kb, kb};
+  for (int a = 0; a < 3; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return WAN_ATTN_EINVAL;
+    for (int b = a + 1; b < 3; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return WAN_ATTN_EINVAL;
+  }
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  WAN_LOG("bwd b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads, (long long)s_q,
+          (long long)s_kv);
+  void* ws = scratch_alloc(wan::attn_bwd_scratch_bytes(sh), st, &rc);
+  if (!ws) return rc;
+  rc = from_hip(wan::launch_attn_bwd(q, k, v, o, d_o, static_cast<const float*>(lse), dq, dk, dv, sh, ws, st),
+                "backward launch");
   hipError_t fe = hipFreeAsync(ws, st);
   if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
   return rc;

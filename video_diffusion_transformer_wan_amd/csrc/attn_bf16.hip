@@ -66,6 +66,7 @@ constexpr float kNeg = -1.0e30f;            // masked score (finite: keeps inf -
 constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 // log2(e) / sqrt(128): scores go straight into exp2
 constexpr float kScaleLog2 = 0.12751743082459868f;
+constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
 constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
 constexpr short kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters untouched
 
@@ -84,6 +85,7 @@ struct Params {
   int split;      // key ranges per query tile (1: the whole key sequence)
   int split_tiles;   // 64-key tiles per key range
   float* ws;      // split > 1: partial results, [item][256][128] O then [item][256][2] (m, l)
+  float* lse;     // optional (may be null): row log-sum-exp of the scaled scores, [b][H][s_q]
 };
 
 __device__ __forceinline__ int swap23(int x) {
@@ -462,6 +464,9 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
     }
     const float inv = 1.0f / (la + lb);
     if (row < p.s_q) {
+      // log-sum-exp of the row's scaled scores: m / sqrt(128) + ln(sum of exp2((s - m) log2(e)/sqrt(128)))
+      if (p.lse != nullptr && h == 0)
+        p.lse[((int64_t)bb * p.heads + hh) * p.s_q + row] = m * kInvSqrtD + logf(la + lb);
       uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
@@ -494,7 +499,7 @@ template <bool kSplit>
 __device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                                           uint16_t* o, int heads, int s_q, int s_kv, int q_tiles,
                                                           int total, int split, int split_tiles, float* ws,
-                                                          int item) {
+                                                          float* lse, int item) {
   Params p;
   p.q = uniform(q);
   p.k = uniform(k);
@@ -510,6 +515,7 @@ __device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, con
   p.split = uniform(split);
   p.split_tiles = uniform(split_tiles);
   p.ws = uniform(ws);
+  p.lse = uniform(lse);
   attn_tile<true, kSplit>(p, uniform(item));
 }
 
@@ -525,7 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
     if (item >= p.total) break;
     if (attn_tile<false, kSplit>(p, item))
       attn_tile_exact<kSplit>(p.q, p.k, p.v, p.o, p.heads, p.s_q, p.s_kv, p.q_tiles, p.total, p.split,
-                              p.split_tiles, p.ws, item);
+                              p.split_tiles, p.ws, p.lse, item);
   }
 }
 
@@ -556,7 +562,8 @@ __global__ __launch_bounds__(256) void attn_bf16_combine_kernel(const Params p) 
   if (lane < p.split) mine = *reinterpret_cast<const f32x2_t*>(ml + 2 * (first + (int64_t)lane * kBM));
   const float mx = wave_max(mine[0]);
   const float w = lane < p.split ? __builtin_amdgcn_exp2f((mine[0] - mx) * kScaleLog2) : 0.0f;
-  const float inv = 1.0f / wave_sum(w * mine[1]);
+  const float total_l = wave_sum(w * mine[1]);
+  const float inv = 1.0f / total_l;
   float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll 8
   for (int sp = 0; sp < p.split; ++sp) {
@@ -568,6 +575,7 @@ __global__ __launch_bounds__(256) void attn_bf16_combine_kernel(const Params p) 
   const int64_t bb = bh / p.heads, hh = bh - bb * p.heads;
   *reinterpret_cast<unsigned*>(p.o + ((bb * p.s_q + i) * p.heads + hh) * kHeadDim + 2 * lane) =
       cvt_pk_bf16(a0 * inv, a1 * inv);
+  if (p.lse != nullptr && lane == 0) p.lse[row] = mx * kInvSqrtD + logf(total_l);
 }
 
 int device_cus() {
@@ -584,7 +592,7 @@ int device_cus() {
 }
 
 Params make_params(const void* q, const void* k, const void* v, void* o, const AttnShape& sh, int split,
-                   void* ws) {
+                   void* ws, float* lse) {
   Params p;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
@@ -598,6 +606,7 @@ Params make_params(const void* q, const void* k, const void* v, void* o, const A
   p.split = split;
   p.split_tiles = (int)ceil_div(n_kt, split);
   p.ws = static_cast<float*>(ws);
+  p.lse = lse;
   p.total = (int)(p.q_tiles * sh.batch * sh.heads * split);
   p.per_xcd = (int)ceil_div(p.total, 8);
   // one workgroup per CU (the LDS ring and the registers allow no second one)
@@ -608,9 +617,9 @@ Params make_params(const void* q, const void* k, const void* v, void* o, const A
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             const AttnShape& sh, hipStream_t stream) {
-  const Params p = make_params(q, k, v, o, sh, 1, nullptr);
+  const Params p = make_params(q, k, v, o, sh, 1, nullptr, lse);
   hipLaunchKernelGGL(attn_fwd_bf16_kernel<false>, dim3((unsigned)(8 * p.n_slots)), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
@@ -634,9 +643,9 @@ size_t attn_bf16_split_bytes(const AttnShape& sh, int split) {
   return (size_t)items * kBM * (kHeadDim + 2) * sizeof(float);
 }
 
-hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o,
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse,
                                   const AttnShape& sh, int split, void* ws, hipStream_t stream) {
-  const Params p = make_params(q, k, v, o, sh, split, ws);
+  const Params p = make_params(q, k, v, o, sh, split, ws, lse);
   hipLaunchKernelGGL(attn_fwd_bf16_kernel<true>, dim3((unsigned)(8 * p.n_slots)), dim3(kThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

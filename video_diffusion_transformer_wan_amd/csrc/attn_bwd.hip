@@ -1,0 +1,467 @@
+// bf16 attention backward for gfx950 (MI355X): dQ, dK and dV of O = softmax(Q K^T / sqrt(128)) V,
+// non-causal, per (batch, head).  The backward of non-causal attention is the beta = 8 term of the
+// DiT cost model and the bulk of training time at long sequences ("Wan 2.1: VBench 86.22% ..."
+// explainer of the Wan technical report, section "先看现象").  With P = exp(S - lse) recomputed from
+// the forward's row log-sum-exp, D_i = rowsum(dO_i * O_i) and dS = P * (dP - D):
+//     dV = P^T dO,   dP = dO V^T,   dQ = dS K / sqrt(128),   dK = dS^T Q / sqrt(128)
+// (the chain rule through the row softmax; D_i = sum_j P_ij dP_ij = dO_i . O_i).
+//
+// Kernels:
+//  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) and dsum = rowsum(dO * O) per query row, f32,
+//    [b*H][s_q padded to 64]; padding rows get lse2 = 1e30 (so P = 0) and dsum = 0.
+//  * attn_bwd_dq_kernel -- one workgroup = 4 waves = 128 query rows of one (batch, head); each lane
+//    owns one query row (transposed products, as in the forward):
+//        S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
+//        dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
+//    looping over 64-key tiles of K and V streamed through a 2-stage LDS ring.
+//  * attn_bwd_dkdv_kernel -- one workgroup = 4 waves = 128 keys; each lane owns one key:
+//        S = Q K^T,  dP = dO V^T        (A = Q, dO rows from LDS; B = K^T, V^T in VGPRs)
+//        dV^T += dO^T P,  dK^T += Q^T dS  (A by transposing LDS reads; B = P, dS from VGPRs)
+//    looping over 64-query tiles of Q, dO and the row statistics.
+// Rows read as MFMA A operands go through a read-time permutation (bits 2 and 3 of the row index
+// swapped inside each 32-row block) so that the 8 values a lane feeds a later MFMA from its
+// accumulators belong to 8 consecutive rows; the transposing reads (ds_read_b64_tr_b16) hand
+// each lane one channel of 4 consecutive rows.  Tiles are stored with 16-byte chunk c of row r at
+// chunk c ^ sigma(r % 16), sigma swapping the two 2-bit fields: conflict-free for both the row
+// reads and the transposing reads.
+
+#include "wan_attn_internal.h"
+
+namespace wan {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;             // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
+constexpr int kTile = 64;                      // rows per streamed LDS tile
+constexpr int kTileBytes = kTile * kHeadDim * 2;   // 16 KB
+constexpr int kStatBytes = 2048;               // lse2 (1 KB) and dsum (1 KB) of a query tile
+constexpr float kScaleLog2 = 0.12751743082459868f;   // log2(e) / sqrt(128)
+constexpr float kInvSqrtD = 0.08838834764831845f;    // 1 / sqrt(128)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kPadLse2 = 1.0e30f;            // exp2(s * kScaleLog2 - kPadLse2) == 0
+constexpr float kNeg = -1.0e30f;
+constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* d_o;
+  const float* lse;   // [b*H][s_q]
+  float* lse2;        // [b*H][s_q_pad]
+  float* dsum;        // [b*H][s_q_pad]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  int heads, s_q, s_kv, s_q_pad;
+  int q_blocks;       // 128-row query blocks per (b, h)  (dQ kernel)
+  int k_blocks;       // 128-key blocks per (b, h)        (dK/dV kernel)
+};
+
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+__device__ __forceinline__ int sigma16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// byte offset of logical 16-byte chunk `chunk` of tile row `row`
+__device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + 16 * (chunk ^ sigma16(row & 15)); }
+
+__device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, r);
+}
+__device__ __forceinline__ float bf16_lo(unsigned x) { return __builtin_bit_cast(float, x << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
+
+__device__ __forceinline__ int clamp_bytes(int64_t bytes) {
+  return bytes <= 0 ? 0 : (bytes >= 0x7fffffffLL ? 0x7fffffff : (int)bytes);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, clamp_bytes(bytes), (int)kRsrcFlags);
+}
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const u32x4_t r = {(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, (unsigned)clamp_bytes(bytes), kRsrcFlags};
+  return r;
+}
+// Direct global -> LDS load of 16 bytes per lane to lds_addr + 16 * lane (bytes past the buffer's
+// end read as zeros).  Inline asm, so that the compiler adds no wait for it before unrelated LDS
+// reads; every wait for these loads is explicit (the workgroup barrier at the end of a tile).
+__device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
+}
+
+// One row-major 64 x 128 bf16 tile from global memory (rows `stride` bytes apart, `bytes` readable
+// from `base`) into LDS at `lds`: wave wv writes 1 KB blocks 4wv .. 4wv+3, lane i the 16 bytes at
+// block + 16 i, i.e. tile row 4 * block + i / 16, stored chunk i % 16, which holds logical chunk
+// (i % 16) ^ sigma(row % 16).
+__device__ __forceinline__ void load_tile(const unsigned char* base, int64_t bytes, int64_t stride,
+                                          unsigned lds, int wv, int lane) {
+  const u32x4_t r = rsrc_words(base, bytes);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int blk = 4 * wv + it;
+    const int row = 4 * blk + (lane >> 4);
+    const int chunk = (lane & 15) ^ sigma16(row & 15);
+    dma_b128(r, lds + 1024 * blk, (unsigned)(row * stride + 16 * chunk));
+  }
+}
+
+// A operand rows (32 x 16 channels) of MFMA step c for rows 32 rb .. 32 rb + 31 of a tile: lane
+// reads tile row 32 rb + swap23(l32), channels 16c + 8h .. +7.
+__device__ __forceinline__ bf16x8_t read_rows(const unsigned char* tile, int rb, int c, int l32, int h) {
+  return *reinterpret_cast<const bf16x8_t*>(tile + tile_off(32 * rb + swap23(l32), 2 * c + h));
+}
+
+// A operand of a product that reduces over tile rows: 32 channels (32 db .. 32 db + 31) x 16 tile
+// rows (16 t .. 16 t + 15), by two transposing reads.  Within each 16-lane group, lane 4 kq + q
+// addresses row kq of 4 consecutive rows and channels 4q .. 4q+3 of the group's 16-channel slice;
+// lane l32 receives channel 32 db + l32 of rows 16 t + 8 h + 4 e .. +3 (e = 0, 1).
+__device__ __forceinline__ bf16x8_t read_cols(const unsigned char* tile, int t, int db, int lane) {
+  const int g4 = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
+  i16x4_t part[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int row = 16 * t + 8 * (g4 >> 1) + 4 * e + kq;
+    const int off = tile_off(row, 4 * db + 2 * (g4 & 1) + (q >> 1)) + 8 * (q & 1);
+    part[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(tile + off));
+  }
+  return __builtin_bit_cast(bf16x8_t, part);
+}
+
+// Wait for this wave's direct-to-LDS loads (the compiler does not track the inline-asm loads, so
+// the wait is explicit: s_waitcnt vmcnt(0), other counters untouched), then the workgroup barrier:
+// after it every wave's loads have landed and every wave is done with the tile it read before.
+__device__ __forceinline__ void barrier_all() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stage 1: lse2 and dsum per query row; 8 lanes per row (16 channels each), rows in [b*H][s_q_pad]
+// order.
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, int64_t total) {
+  const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  if (r >= total) return;   // the 8 lanes of a row leave together
+  const int64_t bh = r / p.s_q_pad;
+  const int i = (int)(r - bh * p.s_q_pad);
+  float acc = 0.0f;
+  if (i < p.s_q) {
+    const int64_t b = bh / p.heads, h = bh - b * p.heads;
+    const int64_t tok = ((b * p.s_q + i) * p.heads + h) * kHeadDim + 16 * sub;
+    const u32x4_t* po = reinterpret_cast<const u32x4_t*>(p.o + tok);
+    const u32x4_t* pg = reinterpret_cast<const u32x4_t*>(p.d_o + tok);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const u32x4_t a = po[w], g = pg[w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += bf16_lo(a[e]) * bf16_lo(g[e]) + bf16_hi(a[e]) * bf16_hi(g[e]);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (sub == 0) {
+    p.dsum[r] = acc;
+    p.lse2[r] = i < p.s_q ? p.lse[bh * p.s_q + i] * kLog2e : kPadLse2;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stage 2a: dQ.
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * kTileBytes];   // [stage][K | V]
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int bh = blockIdx.x / p.q_blocks;
+  const int qblk = blockIdx.x - bh * p.q_blocks;
+  const int bb = bh / p.heads, hh = bh - bb * p.heads;
+  const int64_t stride = (int64_t)p.heads * kHeadDim * 2;
+  const int q0 = qblk * kRows + 32 * wv;
+  const int qrow = q0 + l32;
+  const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
+
+  // Q^T and dO^T operands: lane holds row qrow, channels 16c + 8h .. +7 (rows past s_q read zero)
+  const int64_t qoff = ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2 + q0 * stride;
+  const int64_t qbytes = (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t qr = make_rsrc(reinterpret_cast<const unsigned char*>(p.q) + qoff, qbytes);
+  const __amdgpu_buffer_rsrc_t gr = make_rsrc(reinterpret_cast<const unsigned char*>(p.d_o) + qoff, qbytes);
+  bf16x8_t qf[8], gf[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const unsigned off = (unsigned)(l32 * stride + 32 * c + 16 * h);
+    qf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
+    gf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
+  }
+  const float lse2 = qrow < p.s_q ? p.lse2[(int64_t)bh * p.s_q_pad + qrow] : kPadLse2;
+  const float dsum = qrow < p.s_q ? p.dsum[(int64_t)bh * p.s_q_pad + qrow] : 0.0f;
+
+  const int64_t kvoff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kvoff;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kvoff;
+  const int64_t kvbytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;
+  const int n_kt = (p.s_kv + kTile - 1) / kTile;
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)j * kTile * stride;
+    const unsigned st = lds + (unsigned)((j & 1) * 2 * kTileBytes);
+    load_tile(kbase + off, kvbytes - off, stride, st, wv, lane);
+    load_tile(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
+  };
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+
+  issue(0);
+  barrier_all();
+  for (int j = 0; j < n_kt; ++j) {
+    if (j + 1 < n_kt) issue(j + 1);   // stage (j+1) & 1: free since the barrier that ended tile j-1
+    const unsigned char* ks = smem + (j & 1) * 2 * kTileBytes;
+    const unsigned char* vs = ks + kTileBytes;
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(ks, kb, c, l32, h), qf[c], s[kb], 0, 0, 0);
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(vs, kb, c, l32, h), gf[c], dp[kb], 0, 0, 0);
+      }
+    // register r of key block kb holds key 64 j + 32 kb + 16 (r / 8) + 8 h + r % 8 of this lane's row
+    unsigned ds[2][8];
+    const int kv0 = j * kTile;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float sa = s[kb][r], sb = s[kb][r + 1];
+        if (kv0 + kTile > p.s_kv) {
+          const int key = kv0 + 32 * kb + 16 * (r >> 3) + 8 * h + (r & 7);
+          if (key >= p.s_kv) sa = kNeg;
+          if (key + 1 >= p.s_kv) sb = kNeg;
+        }
+        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sa, kScaleLog2, -lse2));
+        const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sb, kScaleLog2, -lse2));
+        ds[kb][r >> 1] = cvt_pk_bf16(pa * (dp[kb][r] - dsum), pb * (dp[kb][r + 1] - dsum));
+      }
+    // dQ^T += K^T dS^T over the tile's 4 steps of 16 keys
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int kb = t >> 1, u = t & 1;
+      const u32x4_t x = {ds[kb][4 * u], ds[kb][4 * u + 1], ds[kb][4 * u + 2], ds[kb][4 * u + 3]};
+      const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(ks, t, db, lane), bop, acc[db], 0, 0, 0);
+    }
+    barrier_all();   // tile j+1 has landed; every wave is done with stage j & 1
+  }
+
+  // dQ = dQ^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of row qrow
+  if (qrow < p.s_q) {
+    uint16_t* dst = p.dq + (((int64_t)bb * p.s_q + qrow) * p.heads + hh) * kHeadDim + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2_t x = {cvt_pk_bf16(acc[db][4 * g] * kInvSqrtD, acc[db][4 * g + 1] * kInvSqrtD),
+                           cvt_pk_bf16(acc[db][4 * g + 2] * kInvSqrtD, acc[db][4 * g + 3] * kInvSqrtD)};
+        *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Stage 2b: dK and dV.
+__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
+  // accumulators live in the AGPRs: the register file holds K^T, V^T, dK^T, dV^T, S, dP and P
+  // only that way (this empty statement lets the compiler use them)
+  asm volatile("" ::: "a0");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (2 * kTileBytes + kStatBytes)];   // [stage][Q | dO | stats]
+  constexpr int kStage = 2 * kTileBytes + kStatBytes;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
+  const int bh = blockIdx.x / p.k_blocks;
+  const int kblk = blockIdx.x - bh * p.k_blocks;
+  const int bb = bh / p.heads, hh = bh - bb * p.heads;
+  const int64_t stride = (int64_t)p.heads * kHeadDim * 2;
+  const int k0 = kblk * kRows + 32 * wv;
+  const int krow = k0 + l32;
+  const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
+
+  // K^T and V^T operands (B of S and dP): lane holds key krow, channels 16c + 8h .. +7
+  const int64_t koff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2 + k0 * stride;
+  const int64_t kbytes = (int64_t)(p.s_kv - 1 - k0) * stride + kHeadDim * 2;
+  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const unsigned char*>(p.k) + koff, kbytes);
+  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const unsigned char*>(p.v) + koff, kbytes);
+  bf16x8_t kf[8], vf[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const unsigned off = (unsigned)(l32 * stride + 32 * c + 16 * h);
+    kf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
+    vf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
+  }
+
+  const int64_t qoff = ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
+  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + qoff;
+  const unsigned char* gbase = reinterpret_cast<const unsigned char*>(p.d_o) + qoff;
+  const int64_t qbytes = (int64_t)(p.s_q - 1) * stride + kHeadDim * 2;
+  const float* lse2 = p.lse2 + (int64_t)bh * p.s_q_pad;
+  const float* dsum = p.dsum + (int64_t)bh * p.s_q_pad;
+  const int n_qt = p.s_q_pad / kTile;
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)i * kTile * stride;
+    const unsigned st = lds + (unsigned)((i & 1) * kStage);
+    load_tile(qbase + off, qbytes - off, stride, st, wv, lane);
+    load_tile(gbase + off, qbytes - off, stride, st + kTileBytes, wv, lane);
+    if (wv == 0) {   // 256 bytes of each statistic: lanes 16..63 repeat lanes 0..15
+      dma_b128(rsrc_words(lse2 + i * kTile, kTile * 4), st + 2 * kTileBytes, (unsigned)(16 * (lane & 15)));
+      dma_b128(rsrc_words(dsum + i * kTile, kTile * 4), st + 2 * kTileBytes + 1024, (unsigned)(16 * (lane & 15)));
+    }
+  };
+
+  f32x16_t dka[4], dva[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.0f;
+
+  issue(0);
+  barrier_all();
+  for (int i = 0; i < n_qt; ++i) {
+    if (i + 1 < n_qt) issue(i + 1);
+    const unsigned char* qs = smem + (i & 1) * kStage;
+    const unsigned char* gs = qs + kTileBytes;
+    const float* st_lse2 = reinterpret_cast<const float*>(qs + 2 * kTileBytes);
+    const float* st_dsum = reinterpret_cast<const float*>(qs + 2 * kTileBytes + 1024);
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(qs, qb, c, l32, h), kf[c], s[qb], 0, 0, 0);
+        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(gs, qb, c, l32, h), vf[c], dp[qb], 0, 0, 0);
+      }
+    // register r of query block qb holds query 64 i + 32 qb + 16 (r / 8) + 8 h + r % 8 (this lane's key)
+    unsigned pp[2][8], ds[2][8];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
+        const f32x4_t la = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0);
+        const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0 + 4);
+        const f32x4_t da = *reinterpret_cast<const f32x4_t*>(st_dsum + row0);
+        const f32x4_t dbv = *reinterpret_cast<const f32x4_t*>(st_dsum + row0 + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int r = 8 * half + e;
+          const float l0 = e < 4 ? la[e] : lb[e - 4], l1 = e < 4 ? la[e + 1] : lb[e - 3];
+          const float d0 = e < 4 ? da[e] : dbv[e - 4], d1 = e < 4 ? da[e + 1] : dbv[e - 3];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], kScaleLog2, -l0));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], kScaleLog2, -l1));
+          pp[qb][r >> 1] = cvt_pk_bf16(p0, p1);
+          ds[qb][r >> 1] = cvt_pk_bf16(p0 * (dp[qb][r] - d0), p1 * (dp[qb][r + 1] - d1));
+        }
+      }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 4 steps of 16 query rows
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int qb = t >> 1, u = t & 1;
+      const u32x4_t xp = {pp[qb][4 * u], pp[qb][4 * u + 1], pp[qb][4 * u + 2], pp[qb][4 * u + 3]};
+      const u32x4_t xs = {ds[qb][4 * u], ds[qb][4 * u + 1], ds[qb][4 * u + 2], ds[qb][4 * u + 3]};
+      const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, xp);
+      const bf16x8_t bs = __builtin_bit_cast(bf16x8_t, xs);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(gs, t, db, lane), bp, dva[db], 0, 0, 0);
+        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(qs, t, db, lane), bs, dka[db], 0, 0, 0);
+      }
+    }
+    barrier_all();
+  }
+
+  if (krow < p.s_kv) {
+    const int64_t off = (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2_t xk = {cvt_pk_bf16(dka[db][4 * g] * kInvSqrtD, dka[db][4 * g + 1] * kInvSqrtD),
+                            cvt_pk_bf16(dka[db][4 * g + 2] * kInvSqrtD, dka[db][4 * g + 3] * kInvSqrtD)};
+        const u32x2_t xv = {cvt_pk_bf16(dva[db][4 * g], dva[db][4 * g + 1]),
+                            cvt_pk_bf16(dva[db][4 * g + 2], dva[db][4 * g + 3])};
+        *reinterpret_cast<u32x2_t*>(p.dk + off + 32 * db + 8 * g) = xk;
+        *reinterpret_cast<u32x2_t*>(p.dv + off + 32 * db + 8 * g) = xv;
+      }
+  }
+}
+
+}  // namespace
+
+size_t attn_bwd_scratch_bytes(const AttnShape& sh) {
+  const size_t s_q_pad = (size_t)ceil_div(sh.s_q, kTile) * kTile;
+  return 2 * (size_t)sh.batch * sh.heads * s_q_pad * sizeof(float);
+}
+
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                           const float* lse, void* dq, void* dk, void* dv, const AttnShape& sh,
+                           void* scratch, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.o = static_cast<const uint16_t*>(o);
+  p.d_o = static_cast<const uint16_t*>(d_o);
+  p.lse = lse;
+  p.heads = (int)sh.heads;
+  p.s_q = (int)sh.s_q;
+  p.s_kv = (int)sh.s_kv;
+  p.s_q_pad = (int)(ceil_div(sh.s_q, kTile) * kTile);
+  const int64_t bh = sh.batch * sh.heads;
+  p.lse2 = static_cast<float*>(scratch);
+  p.dsum = p.lse2 + bh * p.s_q_pad;
+  p.dq = static_cast<uint16_t*>(dq);
+  p.dk = static_cast<uint16_t*>(dk);
+  p.dv = static_cast<uint16_t*>(dv);
+  p.q_blocks = (int)ceil_div(sh.s_q, kRows);
+  p.k_blocks = (int)ceil_div(sh.s_kv, kRows);
+  const int64_t rows = bh * p.s_q_pad;
+  hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)ceil_div(rows, 32)), dim3(256), 0, stream, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(bh * p.q_blocks)), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)(bh * p.k_blocks)), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace wan

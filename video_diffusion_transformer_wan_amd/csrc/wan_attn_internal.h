@@ -13,16 +13,26 @@ struct AttnShape {
   int64_t batch, heads, s_q, s_kv;
 };
 
-// bf16 flash-attention forward: q, k, v, o bf16 [b, s, H, 128].
-hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o,
+// bf16 flash-attention forward: q, k, v, o bf16 [b, s, H, 128]; lse (optional, may be null) f32
+// [b, H, s_q]: the row log-sum-exp of the scaled scores.
+hipError_t launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             const AttnShape& sh, hipStream_t stream);
 // Key ranges per query tile for shapes with too few query tiles to fill the chip (1: none),
 // the scratch bytes that split needs, and the split launch (attention over key ranges, then the
 // combination of the ranges into o).
 int attn_bf16_split(const AttnShape& sh);
 size_t attn_bf16_split_bytes(const AttnShape& sh, int split);
-hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o,
+hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, void* o, float* lse,
                                   const AttnShape& sh, int split, void* ws, hipStream_t stream);
+
+// bf16 attention backward.  Stage 1: the row statistics the gradient kernels read -- lse2 =
+// lse * log2(e) and dsum = rowsum(dO * O), both f32 [b*H][s_q_pad] with s_q_pad = s_q rounded up
+// to 64 (padding rows: lse2 = 1e30, dsum = 0).  Stage 2: dQ, then dK and dV (bf16, the layouts
+// of q and k).
+size_t attn_bwd_scratch_bytes(const AttnShape& sh);
+hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                           const float* lse, void* dq, void* dk, void* dv, const AttnShape& sh,
+                           void* scratch, hipStream_t stream);
 
 // 8-bit path, stage 1: per-channel maxima into `chan_max` ([b, H, 3, 128] f32), then codes and
 // scales (layouts documented in include/wan_attn.h).
