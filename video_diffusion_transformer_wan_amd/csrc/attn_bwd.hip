@@ -140,6 +140,25 @@ __device__ __forceinline__ bf16x8_t read_cols(const unsigned char* tile, int t, 
   return __builtin_bit_cast(bf16x8_t, part);
 }
 
+// Gradient accumulation on the matrix cores with the accumulators pinned to AGPRs: acc[i] +=
+// a[i] * b (32x32x16 bf16 MFMAs), one asm block per step.  The accumulators live across the whole
+// key or query sweep and only MFMAs touch them; written as builtins, the compiler would keep them
+// in the same AGPRs as the S and dP products and copy them out and back every tile.  s_nop 2
+// first: the B operand (and, at the first step, the zeroed accumulators) was just written by the
+// VALU, and an MFMA may read a VGPR only 2 wait states after a VALU write to it.  After the sweep,
+// settle_mfma() waits out the last accumulation before the VALU reads the accumulators.
+__device__ __forceinline__ void mfma4_acc(f32x16_t (&acc)[4], const bf16x8_t (&a)[4], bf16x8_t b) {
+  asm volatile(
+      "s_nop 2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
+      "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3"
+      : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b));
+}
+__device__ __forceinline__ void settle_mfma() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15"); }
+
 // Wait for this wave's direct-to-LDS loads (the compiler does not track the inline-asm loads, so
 // the wait is explicit: s_waitcnt vmcnt(0), other counters untouched), then the workgroup barrier:
 // after it every wave's loads have landed and every wave is done with the tile it read before.
@@ -270,13 +289,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
       const int kb = t >> 1, u = t & 1;
       const u32x4_t x = {ds[kb][4 * u], ds[kb][4 * u + 1], ds[kb][4 * u + 2], ds[kb][4 * u + 3]};
       const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
+      bf16x8_t a[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(ks, t, db, lane), bop, acc[db], 0, 0, 0);
+      for (int db = 0; db < 4; ++db) a[db] = read_cols(ks, t, db, lane);
+      mfma4_acc(acc, a, bop);
     }
     barrier_all();   // tile j+1 has landed; every wave is done with stage j & 1
   }
 
+  settle_mfma();
   // dQ = dQ^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of row qrow
   if (qrow < p.s_q) {
     uint16_t* dst = p.dq + (((int64_t)bb * p.s_q + qrow) * p.heads + hh) * kHeadDim + 4 * h;
@@ -294,9 +315,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
 // ---------------------------------------------------------------------------------------------
 // Stage 2b: dK and dV.
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
-  // accumulators live in the AGPRs: the register file holds K^T, V^T, dK^T, dV^T, S, dP and P
-  // only that way (this empty statement lets the compiler use them)
-  asm volatile("" ::: "a0");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (2 * kTileBytes + kStatBytes)];   // [stage][Q | dO | stats]
   constexpr int kStage = 2 * kTileBytes + kStatBytes;
   const int tid = threadIdx.x;
@@ -399,15 +417,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
       const u32x4_t xs = {ds[qb][4 * u], ds[qb][4 * u + 1], ds[qb][4 * u + 2], ds[qb][4 * u + 3]};
       const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, xp);
       const bf16x8_t bs = __builtin_bit_cast(bf16x8_t, xs);
+      bf16x8_t ag[4], aq[4];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(gs, t, db, lane), bp, dva[db], 0, 0, 0);
-        dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(qs, t, db, lane), bs, dka[db], 0, 0, 0);
+        ag[db] = read_cols(gs, t, db, lane);
+        aq[db] = read_cols(qs, t, db, lane);
       }
+      mfma4_acc(dva, ag, bp);
+      mfma4_acc(dka, aq, bs);
     }
     barrier_all();
   }
 
+  settle_mfma();
   if (krow < p.s_kv) {
     const int64_t off = (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
 #pragma unroll
