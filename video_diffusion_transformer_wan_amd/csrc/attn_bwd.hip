@@ -17,7 +17,9 @@
 //  * attn_bwd_dkdv_kernel -- one workgroup = 4 waves = 128 keys; each lane owns one key:
 //        S = Q K^T,  dP = dO V^T        (A = Q, dO rows from LDS; B = K^T, V^T in VGPRs)
 //        dV^T += dO^T P,  dK^T += Q^T dS  (A by transposing LDS reads; B = P, dS from VGPRs)
-//    looping over 64-query tiles of Q, dO and the row statistics.
+//    looping over 64-query tiles of Q, dO and the row statistics (3-stage LDS ring), software-
+//    pipelined over 32-query blocks: S/dP products of block b+2, softmax of block b+1 and the
+//    dV/dK accumulation of block b are issued together.
 // Rows read as MFMA A operands go through a read-time permutation (bits 2 and 3 of the row index
 // swapped inside each 32-row block) so that the 8 values a lane feeds a later MFMA from its
 // accumulators belong to 8 consecutive rows; the transposing reads (ds_read_b64_tr_b16) hand
@@ -146,9 +148,11 @@ __device__ __forceinline__ bf16x8_t read_cols(const unsigned char* tile, int t, 
 // in the same AGPRs as the S and dP products and copy them out and back every tile.  s_nop 2
 // first: the B operand (and, at the first step, the zeroed accumulators) was just written by the
 // VALU, and an MFMA may read a VGPR only 2 wait states after a VALU write to it.  After the sweep,
-// settle_mfma() waits out the last accumulation before the VALU reads the accumulators.
+// settle_mfma() waits out the last accumulation before the VALU reads the accumulators.  The MFMA
+// blocks are not volatile, so the compiler may interleave them with independent VALU work (a
+// volatile asm statement would end its scheduling region).
 __device__ __forceinline__ void mfma4_acc(f32x16_t (&acc)[4], const bf16x8_t (&a)[4], bf16x8_t b) {
-  asm volatile(
+  asm(
       "s_nop 2\n\t"
       "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
       "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
@@ -157,7 +161,38 @@ __device__ __forceinline__ void mfma4_acc(f32x16_t (&acc)[4], const bf16x8_t (&a
       : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
       : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b));
 }
-__device__ __forceinline__ void settle_mfma() { asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15"); }
+__device__ __forceinline__ void settle_mfma(f32x16_t (&acc)[4]) {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+}
+
+// One step of two independent products with B operands held in AGPRs and the accumulators in
+// VGPRs: c0 += a0 * b0, c1 += a1 * b1 (first step: c = a * b).  s_nop 1 first (an operand
+// copied into place by the VALU may be read by an MFMA 2 wait states later; the nop issues while
+// the matrix core is busy with the previous step).  The VALU may read c only after
+// mfma_results_ready().
+__device__ __forceinline__ void mfma2_first(f32x16_t& c0, f32x16_t& c1, bf16x8_t a0, bf16x8_t a1, bf16x8_t b0,
+                                            bf16x8_t b1) {
+  asm(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %5, 0"
+      : "=&v"(c0), "=&v"(c1)
+      : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
+}
+__device__ __forceinline__ void mfma2(f32x16_t& c0, f32x16_t& c1, bf16x8_t a0, bf16x8_t a1, bf16x8_t b0,
+                                      bf16x8_t b1) {
+  asm(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %3, %5, %1"
+      : "+v"(c0), "+v"(c1)
+      : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
+}
+// 21 wait states between the last MFMA of a product and any VALU read of its results: the asm
+// takes the results as operands, so it sits after that MFMA and before the reads.
+__device__ __forceinline__ void mfma_results_ready(f32x16_t& c0, f32x16_t& c1) {
+  asm("s_nop 15\n\ts_nop 4" : "+v"(c0), "+v"(c1));
+}
 
 // Wait for this wave's direct-to-LDS loads (the compiler does not track the inline-asm loads, so
 // the wait is explicit: s_waitcnt vmcnt(0), other counters untouched), then the workgroup barrier:
@@ -297,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
     barrier_all();   // tile j+1 has landed; every wave is done with stage j & 1
   }
 
-  settle_mfma();
+  settle_mfma(acc);
   // dQ = dQ^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of row qrow
   if (qrow < p.s_q) {
     uint16_t* dst = p.dq + (((int64_t)bb * p.s_q + qrow) * p.heads + hh) * kHeadDim + 4 * h;
@@ -315,8 +350,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
 // ---------------------------------------------------------------------------------------------
 // Stage 2b: dK and dV.
 __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * (2 * kTileBytes + kStatBytes)];   // [stage][Q | dO | stats]
-  constexpr int kStage = 2 * kTileBytes + kStatBytes;
+  constexpr int kStage = 2 * kTileBytes + kStatBytes;   // [Q | dO | stats]
+  constexpr int kRing = 3;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -330,7 +366,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
   const int krow = k0 + l32;
   const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
 
-  // K^T and V^T operands (B of S and dP): lane holds key krow, channels 16c + 8h .. +7
+  // K^T and V^T operands (B of S and dP, held in AGPRs): lane holds key krow, channels 16c + 8h .. +7
   const int64_t koff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2 + k0 * stride;
   const int64_t kbytes = (int64_t)(p.s_kv - 1 - k0) * stride + kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const unsigned char*>(p.k) + koff, kbytes);
@@ -350,9 +386,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
   const float* lse2 = p.lse2 + (int64_t)bh * p.s_q_pad;
   const float* dsum = p.dsum + (int64_t)bh * p.s_q_pad;
   const int n_qt = p.s_q_pad / kTile;
+  auto stage = [&](int i) __attribute__((always_inline)) { return smem + (i % kRing) * kStage; };
+  // Per-lane byte offsets of the operand reads within a tile (read_rows / read_cols with rows
+  // 32 qb + ... and 16 step + ... taken out as immediates), computed once; the empty asm keeps
+  // them in registers instead of being rebuilt from the lane index at every read.
+  int rowoff[8], coloff[8];
+  {
+    const int g4 = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) rowoff[c] = tile_off(swap23(l32), 2 * c + h);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        coloff[2 * db + e] = tile_off(8 * (g4 >> 1) + 4 * e + kq, 4 * db + 2 * (g4 & 1) + (q >> 1)) + 8 * (q & 1);
+    asm volatile("" : "+v"(rowoff[0]), "+v"(rowoff[1]), "+v"(rowoff[2]), "+v"(rowoff[3]), "+v"(rowoff[4]),
+                 "+v"(rowoff[5]), "+v"(rowoff[6]), "+v"(rowoff[7]));
+    asm volatile("" : "+v"(coloff[0]), "+v"(coloff[1]), "+v"(coloff[2]), "+v"(coloff[3]), "+v"(coloff[4]),
+                 "+v"(coloff[5]), "+v"(coloff[6]), "+v"(coloff[7]));
+  }
+  auto rows = [&](const unsigned char* t, int qb, int c) __attribute__((always_inline)) {
+    return *reinterpret_cast<const bf16x8_t*>((t + rowoff[c]) + 8192 * qb);
+  };
+  auto cols = [&](const unsigned char* t, int step, int db) __attribute__((always_inline)) {
+    i16x4_t part[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      part[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((t + coloff[2 * db + e]) + 4096 * step));
+    return __builtin_bit_cast(bf16x8_t, part);
+  };
   auto issue = [&](int i) __attribute__((always_inline)) {
     const int64_t off = (int64_t)i * kTile * stride;
-    const unsigned st = lds + (unsigned)((i & 1) * kStage);
+    const unsigned st = lds + (unsigned)((i % kRing) * kStage);
     load_tile(qbase + off, qbytes - off, stride, st, wv, lane);
     load_tile(gbase + off, qbytes - off, stride, st + kTileBytes, wv, lane);
     if (wv == 0) {   // 256 bytes of each statistic: lanes 16..63 repeat lanes 0..15
@@ -367,69 +432,103 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.0f;
 
-  issue(0);
-  barrier_all();
-  for (int i = 0; i < n_qt; ++i) {
-    if (i + 1 < n_qt) issue(i + 1);
-    const unsigned char* qs = smem + (i & 1) * kStage;
-    const unsigned char* gs = qs + kTileBytes;
-    const float* st_lse2 = reinterpret_cast<const float*>(qs + 2 * kTileBytes);
-    const float* st_dsum = reinterpret_cast<const float*>(qs + 2 * kTileBytes + 1024);
-    f32x16_t s[2], dp[2];
+  // One pipeline step over blocks of 32 query rows (qb = 0, 1 of a tile in LDS at t):
+  //   products S, dP of block b+2  (tile at pt, block pqb): 8 steps of 2 MFMAs -> s_out, d_out
+  //   softmax of block b+1 (s_in, d_in; statistics of tile st, block sqb) -> pp_out, ds_out (VALU)
+  //   accumulation of block b (pp_in, ds_in; tile at at, block aqb): dV^T, dK^T, 4 blocks of 4 MFMAs
+  // written interleaved (MFMA blocks, each followed by a slice of the softmax) so that the VALU
+  // work issues while the matrix core runs.  Register r of an S or dP block holds query
+  // 32 qb + 16 (r / 8) + 8 h + r % 8 of its tile (this lane's key).
+  auto step = [&](const unsigned char* pt, int pqb, f32x16_t& s_out, f32x16_t& d_out, const unsigned char* st,
+                  int sqb, f32x16_t& s_in, f32x16_t& d_in, unsigned (&pp_out)[8], unsigned (&ds_out)[8],
+                  const unsigned char* at, int aqb, const unsigned (&pp_in)[8], const unsigned (&ds_in)[8])
+      __attribute__((always_inline)) {
+    const float* st_lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
+    const float* st_dsum = reinterpret_cast<const float*>(st + 2 * kTileBytes + 1024);
+    f32x4_t lse[4], dsm[4];   // rows 32 sqb + 16 half + 8 h + 4 w .. +3 for (half, w) = (i / 2, i % 2)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[qb][r] = dp[qb][r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(qs, qb, c, l32, h), kf[c], s[qb], 0, 0, 0);
-        dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(gs, qb, c, l32, h), vf[c], dp[qb], 0, 0, 0);
-      }
-    // register r of query block qb holds query 64 i + 32 qb + 16 (r / 8) + 8 h + r % 8 (this lane's key)
-    unsigned pp[2][8], ds[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int row0 = 32 * qb + 16 * half + 8 * h;   // 8 consecutive query rows
-        const f32x4_t la = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0);
-        const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0 + 4);
-        const f32x4_t da = *reinterpret_cast<const f32x4_t*>(st_dsum + row0);
-        const f32x4_t dbv = *reinterpret_cast<const f32x4_t*>(st_dsum + row0 + 4);
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int r = 8 * half + e;
-          const float l0 = e < 4 ? la[e] : lb[e - 4], l1 = e < 4 ? la[e + 1] : lb[e - 3];
-          const float d0 = e < 4 ? da[e] : dbv[e - 4], d1 = e < 4 ? da[e + 1] : dbv[e - 3];
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r], kScaleLog2, -l0));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][r + 1], kScaleLog2, -l1));
-          pp[qb][r >> 1] = cvt_pk_bf16(p0, p1);
-          ds[qb][r >> 1] = cvt_pk_bf16(p0 * (dp[qb][r] - d0), p1 * (dp[qb][r + 1] - d1));
-        }
-      }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 4 steps of 16 query rows
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int qb = t >> 1, u = t & 1;
-      const u32x4_t xp = {pp[qb][4 * u], pp[qb][4 * u + 1], pp[qb][4 * u + 2], pp[qb][4 * u + 3]};
-      const u32x4_t xs = {ds[qb][4 * u], ds[qb][4 * u + 1], ds[qb][4 * u + 2], ds[qb][4 * u + 3]};
-      const bf16x8_t bp = __builtin_bit_cast(bf16x8_t, xp);
-      const bf16x8_t bs = __builtin_bit_cast(bf16x8_t, xs);
-      bf16x8_t ag[4], aq[4];
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        ag[db] = read_cols(gs, t, db, lane);
-        aq[db] = read_cols(qs, t, db, lane);
-      }
-      mfma4_acc(dva, ag, bp);
-      mfma4_acc(dka, aq, bs);
+    for (int i = 0; i < 4; ++i) {
+      const int row0 = 32 * sqb + 16 * (i >> 1) + 8 * h + 4 * (i & 1);
+      lse[i] = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0);
+      dsm[i] = *reinterpret_cast<const f32x4_t*>(st_dsum + row0);
     }
-    barrier_all();
+    // softmax slice k: S/dP registers 2k, 2k+1
+    auto soft = [&](int k) __attribute__((always_inline)) {
+      const int r = 2 * k;
+      const float l0 = lse[r >> 2][r & 3], l1 = lse[r >> 2][(r & 3) + 1];
+      const float d0 = dsm[r >> 2][r & 3], d1 = dsm[r >> 2][(r & 3) + 1];
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[r], kScaleLog2, -l0));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[r + 1], kScaleLog2, -l1));
+      pp_out[k] = cvt_pk_bf16(p0, p1);
+      ds_out[k] = cvt_pk_bf16(p0 * (d_in[r] - d0), p1 * (d_in[r + 1] - d1));
+    };
+    // operand rings, filled one MFMA block ahead of use (the MFMA blocks keep the source order)
+    bf16x8_t rq[2], rg[2], ca[2][4];
+    auto ld_rows = [&](int c) __attribute__((always_inline)) {
+      rq[c & 1] = rows(pt, pqb, c);
+      rg[c & 1] = rows(pt + kTileBytes, pqb, c);
+    };
+    // accumulation block m: (u, which) = (m / 2, m % 2): dV (which 0) or dK (which 1), rows 16 (2 aqb + u)
+    auto ld_cols = [&](int m) __attribute__((always_inline)) {
+      const int stp = 2 * aqb + (m >> 1);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) ca[m & 1][db] = cols((m & 1) ? at : at + kTileBytes, stp, db);
+    };
+    auto acc = [&](int m) __attribute__((always_inline)) {
+      const int u = m >> 1;
+      const u32x4_t x = (m & 1) ? u32x4_t{ds_in[4 * u], ds_in[4 * u + 1], ds_in[4 * u + 2], ds_in[4 * u + 3]}
+                                : u32x4_t{pp_in[4 * u], pp_in[4 * u + 1], pp_in[4 * u + 2], pp_in[4 * u + 3]};
+      if (m & 1) mfma4_acc(dka, ca[m & 1], __builtin_bit_cast(bf16x8_t, x));
+      else mfma4_acc(dva, ca[m & 1], __builtin_bit_cast(bf16x8_t, x));
+    };
+    auto prod = [&](int c) __attribute__((always_inline)) {
+      if (c == 0) mfma2_first(s_out, d_out, rq[0], rg[0], kf[0], vf[0]);
+      else mfma2(s_out, d_out, rq[c & 1], rg[c & 1], kf[c], vf[c]);
+    };
+    ld_rows(0); ld_cols(0);
+    ld_rows(1); prod(0); soft(0);
+    ld_cols(1); acc(0);
+    ld_rows(2); prod(1); soft(1);
+    ld_rows(3); prod(2); soft(2);
+    ld_cols(2); acc(1);
+    ld_rows(4); prod(3); soft(3);
+    ld_rows(5); prod(4); soft(4);
+    ld_cols(3); acc(2);
+    ld_rows(6); prod(5); soft(5);
+    ld_rows(7); prod(6); soft(6);
+    acc(3);
+    prod(7); soft(7);
+    mfma_results_ready(s_out, d_out);
+  };
+
+  // Software pipeline over the blocks b = 2i + qb of query tile i: the step of block b issues the
+  // products of block b+2, the softmax of block b+1 and the accumulation of block b.  Tile i sits in
+  // stage i % 3; tile i+2 is loaded while tiles i and i+1 are read.  The products and softmax past
+  // the last block read a stage holding an earlier tile (in bounds) and their results go unused;
+  // the accumulation before block 0 runs on P = dS = 0 and adds nothing.
+  issue(0);
+  if (n_qt > 1) issue(1);
+  barrier_all();
+  f32x16_t sx, dx, sy, dy;
+  unsigned px[8], gx[8], py[8], gy[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) py[k] = gy[k] = 0u;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sx[r] = dx[r] = 0.0f;   // read by the first step's (discarded) softmax
+  // prologue: products of blocks 0 and 1, softmax of block 0 (the accumulations add zeros)
+  step(stage(0), 0, sy, dy, stage(0), 0, sx, dx, px, gx, stage(0), 0, py, gy);   // products of block 0
+  step(stage(0), 1, sx, dx, stage(0), 0, sy, dy, px, gx, stage(0), 0, py, gy);   // block 1; softmax of block 0
+  for (int i = 0; i < n_qt; ++i) {
+    if (i + 2 < n_qt) issue(i + 2);   // stage (i+2) % 3, free since the barrier that ended tile i-1
+    const unsigned char* cur = stage(i);
+    const unsigned char* nxt = stage(i + 1);
+    step(nxt, 0, sy, dy, cur, 1, sx, dx, py, gy, cur, 0, px, gx);   // products 2i+2, softmax 2i+1, acc 2i
+    step(nxt, 1, sx, dx, nxt, 0, sy, dy, px, gx, cur, 1, py, gy);   // products 2i+3, softmax 2i+2, acc 2i+1
+    barrier_all();   // tile i+2 has landed; every wave is done with stage i % 3
   }
 
-  settle_mfma();
+  settle_mfma(dka);
+  settle_mfma(dva);
   if (krow < p.s_kv) {
     const int64_t off = (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
 #pragma unroll
