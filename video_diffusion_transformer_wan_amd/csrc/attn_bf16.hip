@@ -17,7 +17,7 @@
 //    lane feeds to one PV MFMA belong to 8 consecutive keys.  V stays in natural [key][channel]
 //    order and ds_read_b64_tr_b16 hands each lane 4 consecutive keys of one channel.
 //  * K and V tiles go straight from HBM to LDS (buffer_load ... lds, out-of-range rows read as
-//    zeros) into a 3-stage ring; both tiles are XOR-swizzled so operand reads are conflict-free.
+//    zeros) into a 4-stage ring; both tiles are XOR-swizzled so operand reads are conflict-free.
 //  * Ping-pong: waves 0-3 and waves 4-7 share the four SIMDs and run half a tile apart.  In each
 //    half-step one group issues MFMAs (S^T of tile j and the PV product of tile j-1) while the
 //    other runs the softmax of its tile on the VALU; a workgroup barrier between half-steps keeps
@@ -67,8 +67,10 @@ constexpr float kSumLimit = 18446744073709551616.0f;   // 2^64
 // log2(e) / sqrt(128): scores go straight into exp2
 constexpr float kScaleLog2 = 0.12751743082459868f;
 constexpr float kInvSqrtD = 0.08838834764831845f;   // 1 / sqrt(128)
+constexpr float kLn2 = 0.6931471805599453f;
 constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
 constexpr short kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters untouched
+constexpr short kWaitLgkm0 = (short)0xC07F;    // s_waitcnt lgkmcnt(0), other counters untouched
 
 struct Params {
   const uint16_t* q;
@@ -121,10 +123,10 @@ __device__ __forceinline__ int clamp_bytes(int64_t bytes) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, clamp_bytes(bytes), (int)kRsrcFlags);
 }
-// The same descriptor as four words, for the inline-asm loads below.
-__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
+// The same descriptor as four words, for the inline-asm loads below (bytes < 2^31).
+__device__ __forceinline__ u32x4_t rsrc_words32(const void* base, unsigned bytes) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const u32x4_t r = {(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, (unsigned)clamp_bytes(bytes), kRsrcFlags};
+  const u32x4_t r = {(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, bytes, kRsrcFlags};
   return r;
 }
 
@@ -142,14 +144,46 @@ __device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsign
 __shared__ __attribute__((aligned(1024))) unsigned char smem[kStages * kStageBytes];
 __shared__ int redo_flag[kWaves];
 
+// The kernel's Params where the launch put them: its only argument, at the start of the
+// kernel-argument segment.
+typedef __attribute__((address_space(4))) const Params kernarg_params_t;
+
+// The fields of *kp, loaded at this point of the program.  The zero index is hidden from the
+// compiler, so it cannot hoist these loads to the kernel's start and hold every field in a scalar
+// register for the whole kernel: the sweep over the keys needs those registers.
+__device__ __forceinline__ Params load_params(kernarg_params_t* kp) {
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  kernarg_params_t& a = kp[z];
+  Params p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.heads = a.heads;
+  p.s_q = a.s_q;
+  p.s_kv = a.s_kv;
+  p.q_tiles = a.q_tiles;
+  p.total = a.total;
+  p.per_xcd = a.per_xcd;
+  p.n_slots = a.n_slots;
+  p.split = a.split;
+  p.split_tiles = a.split_tiles;
+  p.ws = a.ws;
+  p.lse = a.lse;
+  return p;
+}
+
 // Attention of one query tile (256 rows of one (batch, head)), run by the whole workgroup.
-// kExact = false: one sweep against the max of the first 64 keys; writes O and returns false,
-// or returns true (and writes nothing) when some row sum of the tile passed 2^64.
+// kExact = false: one sweep against the max of the first 64 keys; writes O and returns false, or
+// returns true when some row sum of the tile passed 2^64 (O, written regardless, is then invalid
+// and the caller reruns the tile with kExact = true, which overwrites it).
 // kExact = true: one sweep for the row maxima, one softmax sweep against them; writes O.
 // kSplit: work item `item` is key range item % split of query tile item / split; instead of O it
 // writes the unnormalised O, the reference max m and the row sum l of that range to p.ws.
 template <bool kExact, bool kSplit>
-__device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
+__device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) {
+  const Params p = load_params(kp);
   const int tile = kSplit ? item / p.split : item;
   const int k0 = kSplit ? (item - tile * p.split) * p.split_tiles * kBN : 0;   // first key of the range
   const int s_kv = kSplit ? min(p.s_kv - k0, p.split_tiles * kBN) : p.s_kv;    // keys in the range
@@ -199,8 +233,8 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
     const int64_t kv_head = (((int64_t)bb * p.s_kv + k0) * p.heads + hh) * kHeadDim * 2;   // first key of the range
     const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kv_head;
     const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kv_head;
-    uint16_t* obase = p.o + ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim;
-    const int64_t kv_bytes = (int64_t)(s_kv - 1) * stride + kHeadDim * 2;   // last key row ends here
+    const unsigned stride32 = (unsigned)stride;            // < 2^25: heads <= 65536
+    const unsigned tile_bytes = kBN * stride32;             // bytes between consecutive key tiles
 
     // ---- Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7
     // (rows past s_q read as zeros and are never stored)
@@ -215,10 +249,15 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
             bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
     }
 
+    // Tile j's descriptors start at its first key and end after its last valid key row, so rows
+    // past s_kv read as zeros.  32-bit scalars only (a tile spans kBN * stride < 2^31 bytes): the
+    // sweep loop's scalar registers are scarce.
     auto issue_tile = [&](int j) __attribute__((always_inline)) {
-      const int64_t off = (int64_t)j * kBN * stride;
-      const u32x4_t kr = rsrc_words(kbase + off, kv_bytes - off);
-      const u32x4_t vr = rsrc_words(vbase + off, kv_bytes - off);
+      const uint64_t off = (uint64_t)(unsigned)j * tile_bytes;
+      const int rows = min(s_kv - j * kBN, kBN);
+      const unsigned bytes = (unsigned)(rows - 1) * stride32 + kHeadDim * 2;
+      const u32x4_t kr = rsrc_words32(kbase + off, bytes);
+      const u32x4_t vr = rsrc_words32(vbase + off, bytes);
       const unsigned st = lds_ring + (unsigned)((j % kStages) * kStageBytes + 2048 * wv);
       dma_b128(kr, st, k_src[0]);
       dma_b128(kr, st + 1024, k_src[1]);
@@ -307,6 +346,16 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
 #pragma unroll
           for (int db = 0; db < 4; ++db)
             o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][db], bop, o[db], 0, 0, 0);
+        }
+        if (kQK && kPV && i == 0) {
+          // the first step's order: two MFMAs, then the next step's four K reads two at a time
+          // between the last two, so that they start as early as the pipe allows (left to
+          // itself the scheduler can issue three MFMAs first, a wait of two MFMA slots)
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -417,20 +466,6 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
 
     if constexpr (!kExact) {
       sweep(yes, true);
-      {
-        float la, lb;
-        pair_values(l, la, lb);
-        const bool over = !(la + lb <= kSumLimit);
-        // the ballot in converged code: inside the lane-0 branch it would count lane 0's row only
-        const bool wave_over = __any(over);
-        if (lane == 0) redo_flag[wv] = wave_over ? 1 : 0;
-      }
-      __syncthreads();
-      int redo = 0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) redo |= redo_flag[w];
-      __syncthreads();   // every wave has read the flags before they are written again
-      if (__builtin_amdgcn_readfirstlane(redo) != 0) return true;
     } else {
       m_run = kNeg;
       sweep(no, false);
@@ -440,14 +475,18 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
       sweep(yes, false);
     }
 
-    // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row
+    // ---- epilogue: O / l -> bf16; lane owns channels 32db + 8g + 4h .. +3 of its query row.
+    // Written before the overflow vote even on the fast path: when the vote sends the tile to the
+    // exact path, that path rewrites every output written here (same threads, program order), and
+    // O dies before the vote instead of living (spilled) across the exact path's call.
     float la, lb;
     pair_values(l, la, lb);
     const int row = q0 + l32;
+    const Params pe = load_params(kp);   // the output fields, loaded after the sweep
     if constexpr (kSplit) {   // partial result of this key range (the combining kernel divides)
-      if (row < p.s_q) {
+      if (row < pe.s_q) {
         const int64_t r = (int64_t)item * kBM + wv * 32 + l32;
-        float* dst = p.ws + r * kHeadDim + 4 * h;
+        float* dst = pe.ws + r * kHeadDim + 4 * h;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -457,25 +496,43 @@ __device__ __forceinline__ bool attn_tile(const Params& p, const int item) {
           }
         if (h == 0) {
           const f32x2_t ml = {m, la + lb};
-          *reinterpret_cast<f32x2_t*>(p.ws + (int64_t)p.total * kBM * kHeadDim + 2 * r) = ml;
+          *reinterpret_cast<f32x2_t*>(pe.ws + (int64_t)pe.total * kBM * kHeadDim + 2 * r) = ml;
         }
       }
-      return false;
+    } else {
+      const float inv = 1.0f / (la + lb);
+      if (row < pe.s_q) {
+        // log-sum-exp of the row's scaled scores: m / sqrt(128) + ln(sum of exp2((s - m) log2(e)/sqrt(128))),
+        // the sum being >= 1 (the reference row max contributes 1 or more)
+        if (pe.lse != nullptr && h == 0)
+          pe.lse[((int64_t)bb * pe.heads + hh) * pe.s_q + row] = m * kInvSqrtD + __builtin_amdgcn_logf(la + lb) * kLn2;
+        uint16_t* dst = pe.o + (((int64_t)bb * pe.s_q + row) * pe.heads + hh) * kHeadDim + 4 * h;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                         cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+            *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
+          }
+      }
     }
-    const float inv = 1.0f / (la + lb);
-    if (row < p.s_q) {
-      // log-sum-exp of the row's scaled scores: m / sqrt(128) + ln(sum of exp2((s - m) log2(e)/sqrt(128)))
-      if (p.lse != nullptr && h == 0)
-        p.lse[((int64_t)bb * p.heads + hh) * p.s_q + row] = m * kInvSqrtD + logf(la + lb);
-      uint16_t* dst = obase + (int64_t)row * p.heads * kHeadDim + 4 * h;
+
+    if constexpr (!kExact) {   // the overflow vote of the fast path
+      const bool over = !(la + lb <= kSumLimit);
+      // the ballot in converged code: inside the lane-0 branch it would count lane 0's row only
+      const bool wave_over = __any(over);
+      if (lane == 0) redo_flag[wv] = wave_over ? 1 : 0;
+      // LDS-only synchronisation (lgkmcnt, then the barrier): a __syncthreads() fence would also
+      // wait for the O stores just issued
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();
+      int redo = 0;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                       cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-          *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
-        }
+      for (int w = 0; w < kWaves; ++w) redo |= redo_flag[w];
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      barrier();   // every wave has read the flags before they are written again
+      if (__builtin_amdgcn_readfirstlane(redo) != 0) return true;
     }
   }
   return false;
@@ -494,29 +551,11 @@ __device__ __forceinline__ T* uniform(T* x) {
 // The exact path, out of line: it runs only for query tiles whose scores outgrow the first 64
 // keys' maximum by far, and keeping its code out of the kernel body keeps the common path's
 // register allocation and schedule as they are.  Arguments of a device function arrive in
-// VGPRs; each is made uniform again, so that the buffer descriptors stay scalar.
+// VGPRs; both are made uniform again, so that the parameter loads and the buffer descriptors
+// stay scalar.
 template <bool kSplit>
-__device__ __attribute__((noinline)) void attn_tile_exact(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                                          uint16_t* o, int heads, int s_q, int s_kv, int q_tiles,
-                                                          int total, int split, int split_tiles, float* ws,
-                                                          float* lse, int item) {
-  Params p;
-  p.q = uniform(q);
-  p.k = uniform(k);
-  p.v = uniform(v);
-  p.o = uniform(o);
-  p.heads = uniform(heads);
-  p.s_q = uniform(s_q);
-  p.s_kv = uniform(s_kv);
-  p.q_tiles = uniform(q_tiles);
-  p.total = uniform(total);
-  p.per_xcd = 0;
-  p.n_slots = 0;
-  p.split = uniform(split);
-  p.split_tiles = uniform(split_tiles);
-  p.ws = uniform(ws);
-  p.lse = uniform(lse);
-  attn_tile<true, kSplit>(p, uniform(item));
+__device__ __attribute__((noinline)) void attn_tile_exact(kernarg_params_t* kp, int item) {
+  attn_tile<true, kSplit>(uniform(kp), uniform(item));
 }
 
 template <bool kSplit>
@@ -524,14 +563,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
   // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes work items slot, slot +
   // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
   // query tiles of one head in lockstep and read each K/V tile through their shared L2.
+  kernarg_params_t* kp = (kernarg_params_t*)__builtin_amdgcn_kernarg_segment_ptr();
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
     const int item = xcd * p.per_xcd + t_local;
     if (item >= p.total) break;
-    if (attn_tile<false, kSplit>(p, item))
-      attn_tile_exact<kSplit>(p.q, p.k, p.v, p.o, p.heads, p.s_q, p.s_kv, p.q_tiles, p.total, p.split,
-                              p.split_tiles, p.ws, p.lse, item);
+    if (attn_tile<false, kSplit>(kp, item)) attn_tile_exact<kSplit>(kp, item);
   }
 }
 
@@ -565,17 +603,24 @@ __global__ __launch_bounds__(256) void attn_bf16_combine_kernel(const Params p) 
   const float total_l = wave_sum(w * mine[1]);
   const float inv = 1.0f / total_l;
   float a0 = 0.0f, a1 = 0.0f;
-#pragma unroll 8
-  for (int sp = 0; sp < p.split; ++sp) {
-    const float ws = __shfl(w, sp);
-    const f32x2_t x = *reinterpret_cast<const f32x2_t*>(p.ws + (first + (int64_t)sp * kBM) * kHeadDim + 2 * lane);
-    a0 += ws * x[0];
-    a1 += ws * x[1];
+  // in groups of 8 ranges, the group's loads in flight together (the shuffles are convergent, so
+  // the compiler does not unroll a loop of unknown trip count around them itself)
+  for (int sp0 = 0; sp0 < p.split; sp0 += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int sp = sp0 + u;
+      const float ws = __shfl(w, sp & 63);
+      if (sp < p.split) {
+        const f32x2_t x = *reinterpret_cast<const f32x2_t*>(p.ws + (first + (int64_t)sp * kBM) * kHeadDim + 2 * lane);
+        a0 += ws * x[0];
+        a1 += ws * x[1];
+      }
+    }
   }
   const int64_t bb = bh / p.heads, hh = bh - bb * p.heads;
   *reinterpret_cast<unsigned*>(p.o + ((bb * p.s_q + i) * p.heads + hh) * kHeadDim + 2 * lane) =
       cvt_pk_bf16(a0 * inv, a1 * inv);
-  if (p.lse != nullptr && lane == 0) p.lse[row] = mx * kInvSqrtD + logf(total_l);
+  if (p.lse != nullptr && lane == 0) p.lse[row] = mx * kInvSqrtD + __builtin_amdgcn_logf(total_l) * kLn2;
 }
 
 int device_cus() {
