@@ -7,19 +7,21 @@
 // (the chain rule through the row softmax; D_i = sum_j P_ij dP_ij = dO_i . O_i).
 //
 // Kernels:
-//  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) and dsum = rowsum(dO * O) per query row, f32,
-//    [b*H][s_q padded to 64]; padding rows get lse2 = 1e30 (so P = 0) and dsum = 0.
+//  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) and D = rowsum(dO * O) per query row, f32, per
+//    64-row query tile [b*H][s_q_pad / 64][lse2 x 64 | D x 64]; padding rows get lse2 = 1e30 (so
+//    P = 0) and D = 0.
 //  * attn_bwd_dq_kernel -- one workgroup = 4 waves = 128 query rows of one (batch, head); each lane
 //    owns one query row (transposed products, as in the forward):
 //        S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
 //        dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
 //    looping over 64-key tiles of K and V streamed through a 2-stage LDS ring.
-//  * attn_bwd_dkdv_kernel -- one workgroup = 4 waves = 128 keys; each lane owns one key:
-//        S = Q K^T,  dP = dO V^T        (A = Q, dO rows from LDS; B = K^T, V^T in VGPRs)
-//        dV^T += dO^T P,  dK^T += Q^T dS  (A by transposing LDS reads; B = P, dS from VGPRs)
-//    looping over 64-query tiles of Q, dO and the row statistics (3-stage LDS ring), software-
-//    pipelined over 32-query blocks: S/dP products of block b+2, softmax of block b+1 and the
-//    dV/dK accumulation of block b are issued together.
+//  * attn_bwd_dkdv_kernel -- one workgroup = 8 waves = 128 keys; each lane owns one key, and two
+//    waves share each group of 32 keys (and a SIMD):
+//        P wave:  S = Q K^T, P,             dV^T += dO^T P
+//        dS wave: dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS   (P from the P wave through LDS)
+//    (A = Q, dO rows and, by transposing LDS reads, dO^T, Q^T; B = K^T or V^T in VGPRs, P or dS
+//    from VGPRs), looping over 64-query tiles of Q, dO and the row statistics (4-stage LDS ring)
+//    in 32-query blocks; the two waves of a pair alternate between MFMA and VALU phases.
 // Rows read as MFMA A operands go through a read-time permutation (bits 2 and 3 of the row index
 // swapped inside each 32-row block) so that the 8 values a lane feeds a later MFMA from its
 // accumulators belong to 8 consecutive rows; the transposing reads (ds_read_b64_tr_b16) hand
@@ -47,7 +49,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;             // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
 constexpr int kTile = 64;                      // rows per streamed LDS tile
 constexpr int kTileBytes = kTile * kHeadDim * 2;   // 16 KB
-constexpr int kStatBytes = 2048;               // lse2 (1 KB) and dsum (1 KB) of a query tile
+constexpr int kStatBytes = 1024;               // lse2 and D of a query tile (512 bytes, loaded twice)
 constexpr float kScaleLog2 = 0.12751743082459868f;   // log2(e) / sqrt(128)
 constexpr float kInvSqrtD = 0.08838834764831845f;    // 1 / sqrt(128)
 constexpr float kLog2e = 1.4426950408889634f;
@@ -62,8 +64,7 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* d_o;
   const float* lse;   // [b*H][s_q]
-  float* lse2;        // [b*H][s_q_pad]
-  float* dsum;        // [b*H][s_q_pad]
+  float* stats;       // per 64-row query tile: lse2 of its rows, then D: [b*H][s_q_pad / 64][2][64]
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -76,6 +77,10 @@ __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1)
 __device__ __forceinline__ int sigma16(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // byte offset of logical 16-byte chunk `chunk` of tile row `row`
 __device__ __forceinline__ int tile_off(int row, int chunk) { return row * 256 + 16 * (chunk ^ sigma16(row & 15)); }
+// index of lse2 of query row i of (batch, head) bh in BwdParams::stats; D follows 64 floats later
+__device__ __forceinline__ int64_t stat_index(int64_t bh, int s_q_pad, int i) {
+  return bh * s_q_pad * 2 + (int64_t)(i >> 6) * 128 + (i & 63);
+}
 
 __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
   bf16x2_t r;
@@ -105,15 +110,17 @@ __device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsign
 }
 
 // One row-major 64 x 128 bf16 tile from global memory (rows `stride` bytes apart, `bytes` readable
-// from `base`) into LDS at `lds`: wave wv writes 1 KB blocks 4wv .. 4wv+3, lane i the 16 bytes at
-// block + 16 i, i.e. tile row 4 * block + i / 16, stored chunk i % 16, which holds logical chunk
-// (i % 16) ^ sigma(row % 16).
+// from `base`) into LDS at `lds` by a workgroup of kW waves: wave wv writes 1 KB blocks
+// (16 / kW) wv .. (16 / kW) (wv + 1) - 1, lane i the 16 bytes at block + 16 i, i.e. tile row
+// 4 * block + i / 16, stored chunk i % 16, which holds logical chunk (i % 16) ^ sigma(row % 16).
+template <int kW>
 __device__ __forceinline__ void load_tile(const unsigned char* base, int64_t bytes, int64_t stride,
                                           unsigned lds, int wv, int lane) {
+  constexpr int kPer = 16 / kW;
   const u32x4_t r = rsrc_words(base, bytes);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int blk = 4 * wv + it;
+  for (int it = 0; it < kPer; ++it) {
+    const int blk = kPer * wv + it;
     const int row = 4 * blk + (lane >> 4);
     const int chunk = (lane & 15) ^ sigma16(row & 15);
     dma_b128(r, lds + 1024 * blk, (unsigned)(row * stride + 16 * chunk));
@@ -165,35 +172,6 @@ __device__ __forceinline__ void settle_mfma(f32x16_t (&acc)[4]) {
   asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
 }
 
-// One step of two independent products with B operands held in AGPRs and the accumulators in
-// VGPRs: c0 += a0 * b0, c1 += a1 * b1 (first step: c = a * b).  s_nop 1 first (an operand
-// copied into place by the VALU may be read by an MFMA 2 wait states later; the nop issues while
-// the matrix core is busy with the previous step).  The VALU may read c only after
-// mfma_results_ready().
-__device__ __forceinline__ void mfma2_first(f32x16_t& c0, f32x16_t& c1, bf16x8_t a0, bf16x8_t a1, bf16x8_t b0,
-                                            bf16x8_t b1) {
-  asm(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, 0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %3, %5, 0"
-      : "=&v"(c0), "=&v"(c1)
-      : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
-}
-__device__ __forceinline__ void mfma2(f32x16_t& c0, f32x16_t& c1, bf16x8_t a0, bf16x8_t a1, bf16x8_t b0,
-                                      bf16x8_t b1) {
-  asm(
-      "s_nop 1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %2, %4, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %3, %5, %1"
-      : "+v"(c0), "+v"(c1)
-      : "v"(a0), "v"(a1), "a"(b0), "a"(b1));
-}
-// 21 wait states between the last MFMA of a product and any VALU read of its results: the asm
-// takes the results as operands, so it sits after that MFMA and before the reads.
-__device__ __forceinline__ void mfma_results_ready(f32x16_t& c0, f32x16_t& c1) {
-  asm("s_nop 15\n\ts_nop 4" : "+v"(c0), "+v"(c1));
-}
-
 // Wait for this wave's direct-to-LDS loads (the compiler does not track the inline-asm loads, so
 // the wait is explicit: s_waitcnt vmcnt(0), other counters untouched), then the workgroup barrier:
 // after it every wave's loads have landed and every wave is done with the tile it read before.
@@ -201,10 +179,15 @@ __device__ __forceinline__ void barrier_all() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 }
+// Workgroup barrier without any wait (bare s_barrier): the dK/dV kernel waits for its
+// direct-to-LDS loads (s_waitcnt vmcnt) and its LDS writes (kWaitLgkm0) explicitly, where needed.
+// The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+constexpr short kWaitLgkm0 = (short)0xC07F;   // s_waitcnt lgkmcnt(0), other counters untouched
 
 // ---------------------------------------------------------------------------------------------
-// Stage 1: lse2 and dsum per query row; 8 lanes per row (16 channels each), rows in [b*H][s_q_pad]
-// order.
+// Stage 1: lse2 and D (dsum) per query row; 8 lanes per row (16 channels each), rows in
+// [b*H][s_q_pad] order, written to the per-tile layout of BwdParams::stats.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, int64_t total) {
   const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int sub = threadIdx.x & 7;
@@ -228,8 +211,9 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, i
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
   if (sub == 0) {
-    p.dsum[r] = acc;
-    p.lse2[r] = i < p.s_q ? p.lse[bh * p.s_q + i] * kLog2e : kPadLse2;
+    const int64_t x = stat_index(bh, p.s_q_pad, i);
+    p.stats[x] = i < p.s_q ? p.lse[bh * p.s_q + i] * kLog2e : kPadLse2;
+    p.stats[x + 64] = acc;
   }
 }
 
@@ -262,8 +246,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
     qf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, off, 0, 0));
     gf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
   }
-  const float lse2 = qrow < p.s_q ? p.lse2[(int64_t)bh * p.s_q_pad + qrow] : kPadLse2;
-  const float dsum = qrow < p.s_q ? p.dsum[(int64_t)bh * p.s_q_pad + qrow] : 0.0f;
+  const float lse2 = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow)] : kPadLse2;
+  const float dsum = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow) + 64] : 0.0f;
 
   const int64_t kvoff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kvoff;
@@ -273,8 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
   auto issue = [&](int j) __attribute__((always_inline)) {
     const int64_t off = (int64_t)j * kTile * stride;
     const unsigned st = lds + (unsigned)((j & 1) * 2 * kTileBytes);
-    load_tile(kbase + off, kvbytes - off, stride, st, wv, lane);
-    load_tile(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
+    load_tile<kWaves>(kbase + off, kvbytes - off, stride, st, wv, lane);
+    load_tile<kWaves>(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
   };
 
   f32x16_t acc[4];
@@ -348,48 +332,89 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
 }
 
 // ---------------------------------------------------------------------------------------------
-// Stage 2b: dK and dV.
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
-  constexpr int kStage = 2 * kTileBytes + kStatBytes;   // [Q | dO | stats]
-  constexpr int kRing = 3;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRing * kStage];
+// Stage 2b: dK and dV.  One workgroup = 8 waves = 128 keys of one (batch, head).  Waves w and
+// w + 4 (w < 4) own keys 32 w .. 32 w + 31, one key per lane, and share a SIMD.  Wave w (the P
+// wave) computes S = Q K^T, P and dV^T += dO^T P; wave w + 4 (the dS wave) computes dP = dO V^T,
+// dS = P (dP - D) and dK^T += Q^T dS, taking the fp32 P of each block from the P wave through
+// LDS.  Each wave holds one B operand (K^T or V^T) and one accumulator set, so two waves fit on a
+// SIMD, and the pair runs in opposite phases between workgroup barriers: while one wave issues
+// the MFMAs of a 32-query block, the other runs the VALU work of a block (P, or dS).  Per
+// 64-query tile i (blocks 2i and 2i+1), phases 4i .. 4i+3:
+//   4i    P wave: dV += block 2i-1, S of block 2i         dS wave: dS of block 2i-1
+//   4i+1  P wave: P of block 2i (to LDS)                 dS wave: dK += block 2i-1, dP of block 2i
+//   4i+2  P wave: dV += block 2i, S of block 2i+1        dS wave: dS of block 2i
+//   4i+3  P wave: P of block 2i+1 (to LDS)               dS wave: dK += block 2i, dP of block 2i+1
+// then two more phases for block 2n-1.  Q, dO and the row statistics of 64-query tiles stream
+// through a 4-stage LDS ring: tile u is loaded at the start of phase 4u - 10, into the stage of
+// tile u - 4 (last read in phase 4u - 11), and waited for at the end of phase 4u - 1.
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvStage = 2 * kTileBytes + kStatBytes;   // [Q | dO | statistics], 33 KB
+constexpr int kKvRing = 4;
+constexpr int kPBuf = kKvRing * kKvStage;               // P of one 32-query block per wave pair, 4 KB each
+constexpr int kKvLds = kPBuf + 4 * 4096;                // 148 KB
+constexpr int kLoadsPerTile = 5;                        // direct-to-LDS loads per wave per tile
+
+__global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kKvLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool pwave = wv < 4;
+  const int kw = wv & 3;
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int bh = blockIdx.x / p.k_blocks;
   const int kblk = blockIdx.x - bh * p.k_blocks;
   const int bb = bh / p.heads, hh = bh - bb * p.heads;
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;
-  const int k0 = kblk * kRows + 32 * wv;
+  const int k0 = kblk * kRows + 32 * kw;
   const int krow = k0 + l32;
   const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
 
-  // K^T and V^T operands (B of S and dP, held in AGPRs): lane holds key krow, channels 16c + 8h .. +7
+  // B operand of this wave's product: K^T (P wave) or V^T (dS wave); lane holds key krow,
+  // channels 16c + 8h .. +7 (keys past s_kv read as zeros and are never stored)
   const int64_t koff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2 + k0 * stride;
   const int64_t kbytes = (int64_t)(p.s_kv - 1 - k0) * stride + kHeadDim * 2;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const unsigned char*>(p.k) + koff, kbytes);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const unsigned char*>(p.v) + koff, kbytes);
-  bf16x8_t kf[8], vf[8];
+  const __amdgpu_buffer_rsrc_t br =
+      make_rsrc(reinterpret_cast<const unsigned char*>(pwave ? p.k : p.v) + koff, kbytes);
+  bf16x8_t bf[8];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const unsigned off = (unsigned)(l32 * stride + 32 * c + 16 * h);
-    kf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(kr, off, 0, 0));
-    vf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(vr, off, 0, 0));
-  }
+  for (int c = 0; c < 8; ++c)
+    bf[c] = __builtin_bit_cast(
+        bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(br, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
+  // waited for here, before any direct-to-LDS load is issued: the compiler does not see those, and
+  // would otherwise place its wait for these registers inside the tile loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int64_t qoff = ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
   const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) + qoff;
   const unsigned char* gbase = reinterpret_cast<const unsigned char*>(p.d_o) + qoff;
   const int64_t qbytes = (int64_t)(p.s_q - 1) * stride + kHeadDim * 2;
-  const float* lse2 = p.lse2 + (int64_t)bh * p.s_q_pad;
-  const float* dsum = p.dsum + (int64_t)bh * p.s_q_pad;
+  const float* stats = p.stats + stat_index(bh, p.s_q_pad, 0);
   const int n_qt = p.s_q_pad / kTile;
-  auto stage = [&](int i) __attribute__((always_inline)) { return smem + (i % kRing) * kStage; };
-  // Per-lane byte offsets of the operand reads within a tile (read_rows / read_cols with rows
-  // 32 qb + ... and 16 step + ... taken out as immediates), computed once; the empty asm keeps
-  // them in registers instead of being rebuilt from the lane index at every read.
+  auto stage = [&](int i) __attribute__((always_inline)) { return smem + (i % kKvRing) * kKvStage; };
+  // tile i: Q and dO rows (2 + 2 blocks of 1 KB per wave) and the 512 bytes of statistics, which
+  // every wave loads (lanes 32-63 repeating lanes 0-31, the same bytes to the same place) so that
+  // all waves issue the same number of loads per tile
+  auto issue = [&](int i) __attribute__((always_inline)) {
+    const int64_t off = (int64_t)i * kTile * stride;
+    const unsigned st = lds + (unsigned)((i % kKvRing) * kKvStage);
+    load_tile<kKvWaves>(qbase + off, qbytes - off, stride, st, wv, lane);
+    load_tile<kKvWaves>(gbase + off, qbytes - off, stride, st + kTileBytes, wv, lane);
+    dma_b128(rsrc_words(stats + (int64_t)i * 2 * kTile, 2 * kTile * 4), st + 2 * kTileBytes,
+             (unsigned)(16 * (lane & 31)));
+  };
+  // wait until the tile issued before the last `after` tiles has landed (s_waitcnt vmcnt, other
+  // counters untouched)
+  auto wait_tile = [&](int after) __attribute__((always_inline)) {
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerTile));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+
+  // per-lane byte offsets of the operand reads within a tile, computed once (the empty asm keeps
+  // them in registers instead of being rebuilt from the lane index at every read)
   int rowoff[8], coloff[8];
   {
     const int g4 = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
@@ -405,6 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
     asm volatile("" : "+v"(coloff[0]), "+v"(coloff[1]), "+v"(coloff[2]), "+v"(coloff[3]), "+v"(coloff[4]),
                  "+v"(coloff[5]), "+v"(coloff[6]), "+v"(coloff[7]));
   }
+  // A operand rows (read_rows) and transposed columns (read_cols) with the offsets above
   auto rows = [&](const unsigned char* t, int qb, int c) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8_t*>((t + rowoff[c]) + 8192 * qb);
   };
@@ -415,132 +441,172 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dkdv_kernel(const BwdPar
       part[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((t + coloff[2 * db + e]) + 4096 * step));
     return __builtin_bit_cast(bf16x8_t, part);
   };
-  auto issue = [&](int i) __attribute__((always_inline)) {
-    const int64_t off = (int64_t)i * kTile * stride;
-    const unsigned st = lds + (unsigned)((i % kRing) * kStage);
-    load_tile(qbase + off, qbytes - off, stride, st, wv, lane);
-    load_tile(gbase + off, qbytes - off, stride, st + kTileBytes, wv, lane);
-    if (wv == 0) {   // 256 bytes of each statistic: lanes 16..63 repeat lanes 0..15
-      dma_b128(rsrc_words(lse2 + i * kTile, kTile * 4), st + 2 * kTileBytes, (unsigned)(16 * (lane & 15)));
-      dma_b128(rsrc_words(dsum + i * kTile, kTile * 4), st + 2 * kTileBytes + 1024, (unsigned)(16 * (lane & 15)));
-    }
+  // this wave pair's P slot: chunk j (4 floats) of lane l at float 4 (64 j + l)
+  float* pslot = reinterpret_cast<float*>(smem + kPBuf + 4096 * kw);
+
+  // Register r of the S, P, dP or dS block holds query 32 qb + 16 (r / 8) + 8 h + r % 8 of its
+  // tile (this lane's key); its statistics sit at rows 32 qb + 16 (i / 2) + 8 h + 4 (i % 2) .. +3.
+  auto stat4 = [&](const unsigned char* st, int which, int qb, int i) __attribute__((always_inline)) {
+    const float* x = reinterpret_cast<const float*>(st + 2 * kTileBytes) + 64 * which;
+    return *reinterpret_cast<const f32x4_t*>(x + 32 * qb + 16 * (i >> 1) + 8 * h + 4 * (i & 1));
   };
 
-  f32x16_t dka[4], dva[4];
+  f32x16_t acc[4];          // dV^T (P wave) or dK^T (dS wave), 4 blocks of 32 channels
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.0f;
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  f32x16_t prod;            // S (P wave) or dP (dS wave) of the current block
+  unsigned bop[8];          // bf16 P (P wave) or dS (dS wave) of the block awaiting accumulation
+  bf16x8_t pre[4];          // A operands of that accumulation's first step, read ahead
+#pragma unroll
+  for (int k = 0; k < 8; ++k) bop[k] = 0u;
 
-  // One pipeline step over blocks of 32 query rows (qb = 0, 1 of a tile in LDS at t):
-  //   products S, dP of block b+2  (tile at pt, block pqb): 8 steps of 2 MFMAs -> s_out, d_out
-  //   softmax of block b+1 (s_in, d_in; statistics of tile st, block sqb) -> pp_out, ds_out (VALU)
-  //   accumulation of block b (pp_in, ds_in; tile at at, block aqb): dV^T, dK^T, 4 blocks of 4 MFMAs
-  // written interleaved (MFMA blocks, each followed by a slice of the softmax) so that the VALU
-  // work issues while the matrix core runs.  Register r of an S or dP block holds query
-  // 32 qb + 16 (r / 8) + 8 h + r % 8 of its tile (this lane's key).
-  auto step = [&](const unsigned char* pt, int pqb, f32x16_t& s_out, f32x16_t& d_out, const unsigned char* st,
-                  int sqb, f32x16_t& s_in, f32x16_t& d_in, unsigned (&pp_out)[8], unsigned (&ds_out)[8],
-                  const unsigned char* at, int aqb, const unsigned (&pp_in)[8], const unsigned (&ds_in)[8])
-      __attribute__((always_inline)) {
-    const float* st_lse2 = reinterpret_cast<const float*>(st + 2 * kTileBytes);
-    const float* st_dsum = reinterpret_cast<const float*>(st + 2 * kTileBytes + 1024);
-    f32x4_t lse[4], dsm[4];   // rows 32 sqb + 16 half + 8 h + 4 w .. +3 for (half, w) = (i / 2, i % 2)
+  f32x4_t sv[4];            // statistics of the block in prod (lse2 or D), read ahead for the VALU phase
+
+  // MFMA phase: acc += (transposed A tile at at, half aq) x bop over the two 16-query steps of the
+  // block awaiting accumulation (if `accum`), then prod = (rows of the tile at pt, half pq) x bf (if
+  // `product`) and, for the VALU phase after it, statistic `which` of that block from stage st.
+  // All operand reads are issued ahead, in groups that the scheduling barriers keep in this
+  // order: the accumulation steps (whose operands are older) run first, while the product's rows
+  // arrive, so no MFMA waits for a read issued just before it.
+  auto mfma_phase = [&](bool accum, const unsigned char* at, int aq, bool product, const unsigned char* st,
+                        int poff, int which, int pq) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(3);
+    const unsigned char* pt = st + poff;
+    bf16x8_t r0[4], r1[4], c1[4];
+    if (accum) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row0 = 32 * sqb + 16 * (i >> 1) + 8 * h + 4 * (i & 1);
-      lse[i] = *reinterpret_cast<const f32x4_t*>(st_lse2 + row0);
-      dsm[i] = *reinterpret_cast<const f32x4_t*>(st_dsum + row0);
+      for (int db = 0; db < 4; ++db) c1[db] = cols(at, 2 * aq + 1, db);
     }
-    // softmax slice k: S/dP registers 2k, 2k+1
-    auto soft = [&](int k) __attribute__((always_inline)) {
-      const int r = 2 * k;
-      const float l0 = lse[r >> 2][r & 3], l1 = lse[r >> 2][(r & 3) + 1];
-      const float d0 = dsm[r >> 2][r & 3], d1 = dsm[r >> 2][(r & 3) + 1];
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[r], kScaleLog2, -l0));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s_in[r + 1], kScaleLog2, -l1));
-      pp_out[k] = cvt_pk_bf16(p0, p1);
-      ds_out[k] = cvt_pk_bf16(p0 * (d_in[r] - d0), p1 * (d_in[r + 1] - d1));
-    };
-    // operand rings, filled one MFMA block ahead of use (the MFMA blocks keep the source order)
-    bf16x8_t rq[2], rg[2], ca[2][4];
-    auto ld_rows = [&](int c) __attribute__((always_inline)) {
-      rq[c & 1] = rows(pt, pqb, c);
-      rg[c & 1] = rows(pt + kTileBytes, pqb, c);
-    };
-    // accumulation block m: (u, which) = (m / 2, m % 2): dV (which 0) or dK (which 1), rows 16 (2 aqb + u)
-    auto ld_cols = [&](int m) __attribute__((always_inline)) {
-      const int stp = 2 * aqb + (m >> 1);
+    if (product) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) ca[m & 1][db] = cols((m & 1) ? at : at + kTileBytes, stp, db);
-    };
-    auto acc = [&](int m) __attribute__((always_inline)) {
-      const int u = m >> 1;
-      const u32x4_t x = (m & 1) ? u32x4_t{ds_in[4 * u], ds_in[4 * u + 1], ds_in[4 * u + 2], ds_in[4 * u + 3]}
-                                : u32x4_t{pp_in[4 * u], pp_in[4 * u + 1], pp_in[4 * u + 2], pp_in[4 * u + 3]};
-      if (m & 1) mfma4_acc(dka, ca[m & 1], __builtin_bit_cast(bf16x8_t, x));
-      else mfma4_acc(dva, ca[m & 1], __builtin_bit_cast(bf16x8_t, x));
-    };
-    auto prod = [&](int c) __attribute__((always_inline)) {
-      if (c == 0) mfma2_first(s_out, d_out, rq[0], rg[0], kf[0], vf[0]);
-      else mfma2(s_out, d_out, rq[c & 1], rg[c & 1], kf[c], vf[c]);
-    };
-    ld_rows(0); ld_cols(0);
-    ld_rows(1); prod(0); soft(0);
-    ld_cols(1); acc(0);
-    ld_rows(2); prod(1); soft(1);
-    ld_rows(3); prod(2); soft(2);
-    ld_cols(2); acc(1);
-    ld_rows(4); prod(3); soft(3);
-    ld_rows(5); prod(4); soft(4);
-    ld_cols(3); acc(2);
-    ld_rows(6); prod(5); soft(5);
-    ld_rows(7); prod(6); soft(6);
-    acc(3);
-    prod(7); soft(7);
-    mfma_results_ready(s_out, d_out);
+      for (int c = 0; c < 4; ++c) r0[c] = rows(pt, pq, c);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (accum) {
+      const u32x4_t x = {bop[0], bop[1], bop[2], bop[3]};
+      mfma4_acc(acc, pre, __builtin_bit_cast(bf16x8_t, x));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (product) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) r1[c] = rows(pt, pq, 4 + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = stat4(st, which, pq, i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (accum) {
+      const u32x4_t x = {bop[4], bop[5], bop[6], bop[7]};
+      mfma4_acc(acc, c1, __builtin_bit_cast(bf16x8_t, x));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (product) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x16_t zero = {};
+        prod = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[c], bf[c], c == 0 ? zero : prod, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) prod = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[c], bf[4 + c], prod, 0, 0, 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // Software pipeline over the blocks b = 2i + qb of query tile i: the step of block b issues the
-  // products of block b+2, the softmax of block b+1 and the accumulation of block b.  Tile i sits in
-  // stage i % 3; tile i+2 is loaded while tiles i and i+1 are read.  The products and softmax past
-  // the last block read a stage holding an earlier tile (in bounds) and their results go unused;
-  // the accumulation before block 0 runs on P = dS = 0 and adds nothing.
   issue(0);
   if (n_qt > 1) issue(1);
-  barrier_all();
-  f32x16_t sx, dx, sy, dy;
-  unsigned px[8], gx[8], py[8], gy[8];
+  if (n_qt > 2) issue(2);
+  wait_tile(min(n_qt - 1, 2));
+  barrier();
+
+  if (pwave) {
+    // VALU phase: the dO^T operands of this block's first dV step; P of the block (tile at st,
+    // half qb) from prod and its lse2 (sv): fp32 P to the pair's slot, bf16 P to bop
+    auto valu_phase = [&](const unsigned char* st, int qb) __attribute__((always_inline)) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) py[k] = gy[k] = 0u;
+      for (int db = 0; db < 4; ++db) pre[db] = cols(st + kTileBytes, 2 * qb, db);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4_t pv[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) sx[r] = dx[r] = 0.0f;   // read by the first step's (discarded) softmax
-  // prologue: products of blocks 0 and 1, softmax of block 0 (the accumulations add zeros)
-  step(stage(0), 0, sy, dy, stage(0), 0, sx, dx, px, gx, stage(0), 0, py, gy);   // products of block 0
-  step(stage(0), 1, sx, dx, stage(0), 0, sy, dy, px, gx, stage(0), 0, py, gy);   // block 1; softmax of block 0
-  for (int i = 0; i < n_qt; ++i) {
-    if (i + 2 < n_qt) issue(i + 2);   // stage (i+2) % 3, free since the barrier that ended tile i-1
-    const unsigned char* cur = stage(i);
-    const unsigned char* nxt = stage(i + 1);
-    step(nxt, 0, sy, dy, cur, 1, sx, dx, py, gy, cur, 0, px, gx);   // products 2i+2, softmax 2i+1, acc 2i
-    step(nxt, 1, sx, dx, nxt, 0, sy, dy, px, gx, cur, 1, py, gy);   // products 2i+3, softmax 2i+2, acc 2i+1
-    barrier_all();   // tile i+2 has landed; every wave is done with stage i % 3
+      for (int k = 0; k < 8; ++k) {
+        const int r = 2 * k;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(prod[r], kScaleLog2, -sv[r >> 2][r & 3]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(prod[r + 1], kScaleLog2, -sv[r >> 2][(r & 3) + 1]));
+        bop[k] = cvt_pk_bf16(p0, p1);
+        pv[r >> 2][r & 3] = p0;
+        pv[r >> 2][(r & 3) + 1] = p1;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t*>(pslot + 4 * (64 * j + lane)) = pv[j];
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // P is in LDS before the barrier
+    };
+    for (int i = 0; i < n_qt; ++i) {
+      const unsigned char* cur = stage(i);
+      const unsigned char* prv = stage(i + 3);   // tile i - 1
+      mfma_phase(i > 0, prv + kTileBytes, 1, true, cur, 0, 0, 0);
+      barrier();
+      valu_phase(cur, 0);
+      barrier();
+      if (i + 3 < n_qt) issue(i + 3);
+      mfma_phase(true, cur + kTileBytes, 0, true, cur, 0, 0, 1);
+      barrier();
+      valu_phase(cur, 1);
+      wait_tile(min(n_qt - 2 - i, 2));
+      barrier();
+    }
+    mfma_phase(true, stage(n_qt - 1) + kTileBytes, 1, false, smem, 0, 0, 0);
+    barrier();
+    barrier();
+  } else {
+    // VALU phase: dS of the block (tile at st, half qb) from prod (dP), the P wave's fp32 P and D
+    // (sv), to bop; the Q^T operands of this block's first dK step are read meanwhile
+    auto valu_phase = [&](const unsigned char* st, int qb) __attribute__((always_inline)) {
+      f32x4_t pv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const f32x4_t*>(pslot + 4 * (64 * j + lane));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) pre[db] = cols(st, 2 * qb, db);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 2 * k;
+        const float d0 = prod[r] - sv[r >> 2][r & 3], d1 = prod[r + 1] - sv[r >> 2][(r & 3) + 1];
+        bop[k] = cvt_pk_bf16(pv[r >> 2][r & 3] * d0, pv[r >> 2][(r & 3) + 1] * d1);
+      }
+    };
+    for (int i = 0; i < n_qt; ++i) {
+      const unsigned char* cur = stage(i);
+      const unsigned char* prv = stage(i + 3);   // tile i - 1
+      if (i > 0) valu_phase(prv, 1);
+      barrier();
+      mfma_phase(i > 0, prv, 1, true, cur, kTileBytes, 1, 0);
+      barrier();
+      if (i + 3 < n_qt) issue(i + 3);
+      valu_phase(cur, 0);
+      barrier();
+      mfma_phase(true, cur, 0, true, cur, kTileBytes, 1, 1);
+      wait_tile(min(n_qt - 2 - i, 2));
+      barrier();
+    }
+    valu_phase(stage(n_qt - 1), 1);
+    barrier();
+    mfma_phase(true, stage(n_qt - 1), 1, false, smem, 0, 1, 0);
+    barrier();
   }
 
-  settle_mfma(dka);
-  settle_mfma(dva);
+  settle_mfma(acc);
   if (krow < p.s_kv) {
-    const int64_t off = (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
+    // dV = dV^T; dK = dK^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of key krow
+    const float scale = pwave ? 1.0f : kInvSqrtD;
+    uint16_t* dst = (pwave ? p.dv : p.dk) + (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x2_t xk = {cvt_pk_bf16(dka[db][4 * g] * kInvSqrtD, dka[db][4 * g + 1] * kInvSqrtD),
-                            cvt_pk_bf16(dka[db][4 * g + 2] * kInvSqrtD, dka[db][4 * g + 3] * kInvSqrtD)};
-        const u32x2_t xv = {cvt_pk_bf16(dva[db][4 * g], dva[db][4 * g + 1]),
-                            cvt_pk_bf16(dva[db][4 * g + 2], dva[db][4 * g + 3])};
-        *reinterpret_cast<u32x2_t*>(p.dk + off + 32 * db + 8 * g) = xk;
-        *reinterpret_cast<u32x2_t*>(p.dv + off + 32 * db + 8 * g) = xv;
+        const u32x2_t x = {cvt_pk_bf16(acc[db][4 * g] * scale, acc[db][4 * g + 1] * scale),
+                           cvt_pk_bf16(acc[db][4 * g + 2] * scale, acc[db][4 * g + 3] * scale)};
+        *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
       }
   }
 }
@@ -567,8 +633,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   p.s_kv = (int)sh.s_kv;
   p.s_q_pad = (int)(ceil_div(sh.s_q, kTile) * kTile);
   const int64_t bh = sh.batch * sh.heads;
-  p.lse2 = static_cast<float*>(scratch);
-  p.dsum = p.lse2 + bh * p.s_q_pad;
+  p.stats = static_cast<float*>(scratch);
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
@@ -581,7 +646,7 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(bh * p.q_blocks)), dim3(kThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)(bh * p.k_blocks)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)(bh * p.k_blocks)), dim3(kKvThreads), 0, stream, p);
   return hipGetLastError();
 }
 
