@@ -23,6 +23,9 @@ Modules:
   backward  -- the exact gradients dQ, dK, dV (chain rule through the row softmax) and the row
                log-sum-exp, in float64: the attention backward (beta = 8 term of the cost model,
                same explainer, section "先看现象").
+  fp8_gemm  -- the FP8 GEMM of the DiT linear layers (per-token activation and per-tensor weight
+               e4m3fn quantisation, exact product): "Wan模型是什么它能做什么" explainer,
+               section 4.2.
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py``.  The product path (the HIP library and its Python binding) never imports, links or
