@@ -1,5 +1,6 @@
 /*
- * wan_attn.h -- C ABI of the MI355X (gfx950) attention forward for Wan video DiT blocks.
+ * wan_attn.h -- C ABI of the MI355X (gfx950) attention forward for Wan video DiT blocks (and of the
+ * attention backward and the FP8 GEMM of the DiT linear layers, declared further below).
  *
  * Operation (every entry point below computes it, or a stage of it):
  *   O[b, i, h, :] = sum_j softmax_j( Q[b,i,h,:] . K[b,j,h,:] / sqrt(head_dim) ) * V[b, j, h, :]
@@ -54,7 +55,7 @@ enum wan_attn_status {
   WAN_ATTN_EALIGN = -2,        /* a pointer is not 16-byte aligned                            */
   WAN_ATTN_ENOMEM = -3,        /* scratch allocation failed                                   */
   WAN_ATTN_ELAUNCH = -4,       /* the HIP runtime refused a launch or a query                 */
-  WAN_ATTN_EUNSUPPORTED = -5   /* head_dim other than 128                                     */
+  WAN_ATTN_EUNSUPPORTED = -5   /* head_dim other than 128; an FP8 GEMM size outside its limits */
 };
 
 /*
@@ -138,6 +139,35 @@ int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  const void* lse, void* dq, void* dk, void* dv,
                  int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim,
                  void* stream);
+
+/*
+ * FP8 GEMM of the DiT linear layers (the alpha term of the cost model): Y = X W^T in FP8 with the
+ * activations quantised per token and the weights per tensor ("Wan模型是什么它能做什么"
+ * explainer, section 4.2, where every matrix multiplication of the linear layers runs this way).
+ * Codes are OCP e4m3fn (max 448); for a row (activations) or the whole tensor (weights):
+ *   amax = max |x|,  inv = 448 / amax,  code = e4m3fn( clamp(x * inv, -448, 448) )  (round to nearest
+ *   even, the product taken in fp32),  scale = amax / 448;  amax = 0 gives inv = scale = 1.
+ * Product: Y[m, n] = bf16( (sum_k X~[m, k] * W~[n, k]) * scale_x[m] * scale_w ), the products of the
+ * FP8 values accumulated in fp32 on the matrix cores.  No bias.
+ * Layouts: row-major, dense, device memory.  x [rows, cols] and w [rows, cols] bf16; codes uint8 with
+ * the same shape; y [m, n] bf16.  Sizes: rows >= 1; cols (the reduced dimension k) a multiple of 64,
+ * at most 2^20 (else WAN_ATTN_EUNSUPPORTED); for the GEMM also n a multiple of 4
+ * (WAN_ATTN_EUNSUPPORTED).  Tensors and codes 16-byte aligned, scales 4-byte aligned
+ * (WAN_ATTN_EALIGN).  Outputs must not overlap the inputs (WAN_ATTN_EINVAL).  No scratch memory.
+ */
+
+/* Per-token quantisation of x [rows, cols] bf16: codes [rows, cols] uint8, scales [rows] f32. */
+int wan_fp8_quantize_rows(const void* x, int64_t rows, int64_t cols, void* codes, void* scales,
+                          void* stream);
+
+/* Per-tensor quantisation of w [rows, cols] bf16: codes [rows, cols] uint8 and one f32 scale at
+ * `scale` (the word also holds the running amax while the call's kernels run on `stream`). */
+int wan_fp8_quantize_tensor(const void* w, int64_t rows, int64_t cols, void* codes, void* scale,
+                            void* stream);
+
+/* y [m, n] bf16 = (x_codes [m, k] . w_codes [n, k]^T) * x_scales[m] * (*w_scale), as above. */
+int wan_fp8_gemm(const void* x_codes, const void* x_scales, const void* w_codes, const void* w_scale,
+                 void* y, int64_t m, int64_t n, int64_t k, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* wan_attn_strerror(int code);

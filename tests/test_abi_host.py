@@ -17,13 +17,13 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(wan_attn\w*)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(wan_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
     lib = ensure_built()
     names = declared_functions()
-    assert "wan_attn_fwd" in names and len(names) >= 6
+    assert "wan_attn_fwd" in names and "wan_fp8_gemm" in names and len(names) >= 11
     for n in names:
         assert hasattr(lib, n), n
 
@@ -130,3 +130,51 @@ def test_forward_lse_argument_checks(args, code):
     lib = ensure_built()
     assert lib.wan_attn_fwd_lse(*args, 1, 1, 1, 1, 128, None) == code
     assert lib.wan_attn_fwd_lse(16, 32, 48, 4096, 8192, 1, 1, 1, 1, 96, None) == wan.WAN_ATTN_EUNSUPPORTED
+
+
+def _fp8(fn, **kw):
+    """The FP8 entry points with far-apart fake device addresses (never dereferenced: every case
+    fails a check before the first HIP call)."""
+    lib = ensure_built()
+    if fn == "gemm":
+        names = ["xc", "xs", "wc", "ws", "y"]
+        args = {n: 1 << (20 + i) for i, n in enumerate(names)}
+        args.update(m=1, n=4, k=64)
+        args.update(kw)
+        return lib.wan_fp8_gemm(*[args[n] for n in names], args["m"], args["n"], args["k"], None)
+    args = dict(x=1 << 20, rows=1, cols=64, codes=1 << 21, scales=1 << 22)
+    args.update(kw)
+    f = lib.wan_fp8_quantize_rows if fn == "rows" else lib.wan_fp8_quantize_tensor
+    return f(args["x"], args["rows"], args["cols"], args["codes"], args["scales"], None)
+
+
+@pytest.mark.parametrize("fn", ["rows", "tensor"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), wan.WAN_ATTN_EINVAL),
+    (dict(scales=None), wan.WAN_ATTN_EINVAL),
+    (dict(rows=0), wan.WAN_ATTN_EINVAL),
+    (dict(cols=0), wan.WAN_ATTN_EINVAL),
+    (dict(cols=96), wan.WAN_ATTN_EUNSUPPORTED),        # not a multiple of 64
+    (dict(cols=(1 << 20) + 64), wan.WAN_ATTN_EUNSUPPORTED),
+    (dict(x=(1 << 20) + 8), wan.WAN_ATTN_EALIGN),
+    (dict(scales=(1 << 22) + 2), wan.WAN_ATTN_EALIGN),
+    (dict(codes=(1 << 20) + 64), wan.WAN_ATTN_EINVAL),  # codes overlap x
+])
+def test_fp8_quantize_argument_checks(fn, kw, code):
+    assert _fp8(fn, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(y=None), wan.WAN_ATTN_EINVAL),
+    (dict(ws=None), wan.WAN_ATTN_EINVAL),
+    (dict(m=0), wan.WAN_ATTN_EINVAL),
+    (dict(n=0), wan.WAN_ATTN_EINVAL),
+    (dict(n=6), wan.WAN_ATTN_EUNSUPPORTED),            # n not a multiple of 4
+    (dict(k=100), wan.WAN_ATTN_EUNSUPPORTED),
+    (dict(xc=(1 << 20) + 4), wan.WAN_ATTN_EALIGN),
+    (dict(xs=(1 << 21) + 1), wan.WAN_ATTN_EALIGN),
+    (dict(y=1 << 20), wan.WAN_ATTN_EINVAL),            # y overlaps the activation codes
+    (dict(m=1 << 40, n=1 << 30), wan.WAN_ATTN_EINVAL),  # work items beyond 32 bits
+])
+def test_fp8_gemm_argument_checks(kw, code):
+    assert _fp8("gemm", **kw) == code

@@ -49,6 +49,9 @@ _SIGNATURES = {
                                                _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_fwd_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_fp8_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "wan_fp8_quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
+    "wan_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "wan_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_attn_version": (ctypes.c_int, []),
 }
@@ -220,3 +223,66 @@ def attention_backward(q, k, v, o, lse, d_o, stream=None):
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, b, H, s_q, s_kv, d, stream)
     return dq, dk, dv
+
+
+def wan_fp8_quantize_rows(x, rows, cols, codes, scales, stream=None):
+    rc = lib().wan_fp8_quantize_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream))
+    _check(rc, "wan_fp8_quantize_rows")
+
+
+def wan_fp8_quantize_tensor(w, rows, cols, codes, scale, stream=None):
+    rc = lib().wan_fp8_quantize_tensor(_ptr(w), rows, cols, _ptr(codes), _ptr(scale), _stream(stream))
+    _check(rc, "wan_fp8_quantize_tensor")
+
+
+def wan_fp8_gemm(x_codes, x_scales, w_codes, w_scale, y, m, n, k, stream=None):
+    rc = lib().wan_fp8_gemm(_ptr(x_codes), _ptr(x_scales), _ptr(w_codes), _ptr(w_scale), _ptr(y), m, n, k,
+                            _stream(stream))
+    _check(rc, "wan_fp8_gemm")
+
+
+def _check_matrix(name, t):
+    import torch
+    if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2:
+        raise ValueError(f"{name} must be a contiguous 2-d bfloat16 CUDA tensor")
+    return t.shape
+
+
+def fp8_quantize_rows(x, stream=None):
+    """Per-token e4m3fn quantisation of x [m, k] bf16: (codes [m, k] uint8, scales [m] float32)."""
+    import torch
+    m, k = _check_matrix("x", x)
+    codes = torch.empty((m, k), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((m,), dtype=torch.float32, device=x.device)
+    wan_fp8_quantize_rows(x, m, k, codes, scales, stream)
+    return codes, scales
+
+
+def fp8_quantize_tensor(w, stream=None):
+    """Per-tensor e4m3fn quantisation of w [n, k] bf16: (codes [n, k] uint8, scale [1] float32)."""
+    import torch
+    n, k = _check_matrix("w", w)
+    codes = torch.empty((n, k), dtype=torch.uint8, device=w.device)
+    scale = torch.empty((1,), dtype=torch.float32, device=w.device)
+    wan_fp8_quantize_tensor(w, n, k, codes, scale, stream)
+    return codes, scale
+
+
+def fp8_gemm(x_codes, x_scales, w_codes, w_scale, out=None, stream=None):
+    """y [m, n] bf16 = (x_codes [m, k] . w_codes [n, k]^T) * x_scales[m] * w_scale, from the codes and
+    scales of fp8_quantize_rows / fp8_quantize_tensor."""
+    import torch
+    m, k = x_codes.shape
+    n = w_codes.shape[0]
+    if w_codes.shape[1] != k or x_scales.numel() != m or w_scale.numel() != 1:
+        raise ValueError("shapes of codes and scales do not match")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=x_codes.device)
+    wan_fp8_gemm(x_codes, x_scales, w_codes, w_scale, out, m, n, k, stream)
+    return out
+
+
+def fp8_linear(x, w_codes, w_scale, out=None, stream=None):
+    """y = x w^T in FP8 for x [m, k] bf16 and a weight quantised once with fp8_quantize_tensor."""
+    xc, xs = fp8_quantize_rows(x, stream)
+    return fp8_gemm(xc, xs, w_codes, w_scale, out, stream)

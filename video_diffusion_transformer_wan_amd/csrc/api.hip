@@ -151,7 +151,20 @@ Attn8Layout attn8_layout(int64_t b, int64_t H, int64_t s_q, int64_t s_kv) {
   return L;
 }
 
+// FP8 GEMM sizes: rows >= 1; the reduced dimension a positive multiple of 64 (one MFMA step) of
+// at most 2^20 (32-bit tile offsets; and the products stay exactly summable in float64 for the
+// tests); the work-item count of the GEMM within 32 bits.
+int check_fp8_dims(int64_t rows, int64_t cols) {
+  if (rows < 1 || cols < 1) return WAN_ATTN_EINVAL;
+  if (cols % 64 != 0 || cols > (1LL << 20)) return WAN_ATTN_EUNSUPPORTED;
+  if (rows > (1LL << 40)) return WAN_ATTN_EINVAL;
+  return WAN_ATTN_OK;
+}
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
 }  // namespace
+
 
 extern "C" {
 
@@ -164,7 +177,7 @@ const char* wan_attn_strerror(int code) {
     case WAN_ATTN_EALIGN: return "pointer not 16-byte aligned";
     case WAN_ATTN_ENOMEM: return "out of device memory for scratch";
     case WAN_ATTN_ELAUNCH: return "HIP runtime error while launching";
-    case WAN_ATTN_EUNSUPPORTED: return "unsupported head_dim (only 128)";
+    case WAN_ATTN_EUNSUPPORTED: return "unsupported size (head_dim other than 128, or an FP8 GEMM size outside its limits)";
     default: return "unknown status code";
   }
 }
@@ -309,6 +322,57 @@ int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   hipError_t fe = hipFreeAsync(ws, st);
   if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
   return rc;
+}
+
+int wan_fp8_quantize_rows(const void* x, int64_t rows, int64_t cols, void* codes, void* scales, void* stream) {
+  int rc = check_fp8_dims(rows, cols);
+  if (rc) return rc;
+  if (!x || !codes || !scales) return WAN_ATTN_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned4(scales)) return WAN_ATTN_EALIGN;
+  const int64_t xb = rows * cols * 2, cb = rows * cols, sb = rows * 4;
+  if (overlaps(codes, cb, x, xb) || overlaps(scales, sb, x, xb) || overlaps(scales, sb, codes, cb))
+    return WAN_ATTN_EINVAL;
+  WAN_LOG("fp8_quantize_rows rows=%lld cols=%lld", (long long)rows, (long long)cols);
+  return from_hip(wan::launch_fp8_quantize_rows(x, rows, cols, codes, static_cast<float*>(scales),
+                                                static_cast<hipStream_t>(stream)),
+                  "fp8 row quantisation launch");
+}
+
+int wan_fp8_quantize_tensor(const void* w, int64_t rows, int64_t cols, void* codes, void* scale, void* stream) {
+  int rc = check_fp8_dims(rows, cols);
+  if (rc) return rc;
+  if (!w || !codes || !scale) return WAN_ATTN_EINVAL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned4(scale)) return WAN_ATTN_EALIGN;
+  const int64_t wb = rows * cols * 2, cb = rows * cols;
+  if (overlaps(codes, cb, w, wb) || overlaps(scale, 4, w, wb) || overlaps(scale, 4, codes, cb))
+    return WAN_ATTN_EINVAL;
+  WAN_LOG("fp8_quantize_tensor rows=%lld cols=%lld", (long long)rows, (long long)cols);
+  return from_hip(wan::launch_fp8_quantize_tensor(w, rows, cols, codes, static_cast<float*>(scale),
+                                                  static_cast<hipStream_t>(stream)),
+                  "fp8 tensor quantisation launch");
+}
+
+int wan_fp8_gemm(const void* x_codes, const void* x_scales, const void* w_codes, const void* w_scale, void* y,
+                 int64_t m, int64_t n, int64_t k, void* stream) {
+  int rc = check_fp8_dims(m, k);
+  if (rc) return rc;
+  rc = check_fp8_dims(n, k);
+  if (rc) return rc;
+  if (n % 4 != 0) return WAN_ATTN_EUNSUPPORTED;
+  if ((long double)wan::ceil_div(m, 256) * (long double)wan::ceil_div(n, 256) > 2147483000.0L)
+    return WAN_ATTN_EINVAL;
+  if (!x_codes || !x_scales || !w_codes || !w_scale || !y) return WAN_ATTN_EINVAL;
+  if (!aligned16(x_codes) || !aligned16(w_codes) || !aligned16(y) || !aligned4(x_scales) || !aligned4(w_scale))
+    return WAN_ATTN_EALIGN;
+  const int64_t yb = m * n * 2;
+  if (overlaps(y, yb, x_codes, m * k) || overlaps(y, yb, w_codes, n * k) || overlaps(y, yb, x_scales, m * 4) ||
+      overlaps(y, yb, w_scale, 4))
+    return WAN_ATTN_EINVAL;
+  WAN_LOG("fp8_gemm m=%lld n=%lld k=%lld", (long long)m, (long long)n, (long long)k);
+  return from_hip(wan::launch_fp8_gemm(x_codes, static_cast<const float*>(x_scales), w_codes,
+                                       static_cast<const float*>(w_scale), y, m, n, k,
+                                       static_cast<hipStream_t>(stream)),
+                  "fp8 gemm launch");
 }
 
 }  // extern "C"

@@ -26,9 +26,9 @@ hipError_t launch_attn_bf16_split(const void* q, const void* k, const void* v, v
                                   const AttnShape& sh, int split, void* ws, hipStream_t stream);
 
 // bf16 attention backward.  Stage 1: the row statistics the gradient kernels read -- lse2 =
-// lse * log2(e) and dsum = rowsum(dO * O), both f32 [b*H][s_q_pad] with s_q_pad = s_q rounded up
-// to 64 (padding rows: lse2 = 1e30, dsum = 0).  Stage 2: dQ, then dK and dV (bf16, the layouts
-// of q and k).
+// lse * log2(e) and D = rowsum(dO * O), f32, per 64-row query tile [b*H][s_q_pad / 64][lse2 x 64 |
+// D x 64] with s_q_pad = s_q rounded up to 64 (padding rows: lse2 = 1e30, D = 0).  Stage 2: dQ,
+// then dK and dV (bf16, the layouts of q and k).
 size_t attn_bwd_scratch_bytes(const AttnShape& sh);
 hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                            const float* lse, void* dq, void* dk, void* dv, const AttnShape& sh,
@@ -45,6 +45,16 @@ hipError_t launch_attn8_quantize(const void* q, const void* k, const void* v, co
 hipError_t launch_attn8_fwd(const int8_t* q_codes, const float* q_scale, const int8_t* k_codes,
                             const float* k_scale, const uint8_t* v_codes, const float* v_scale,
                             void* o, const AttnShape& sh, hipStream_t stream);
+
+// FP8 GEMM of the linear layers (layouts documented in include/wan_attn.h): per-token codes and
+// scales of x [rows][cols], per-tensor codes and scale of w (the scale word doubles as the amax
+// accumulator until the last kernel), and y [m][n] bf16 = (x~ w~^T) * x_scale[m] * w_scale.
+hipError_t launch_fp8_quantize_rows(const void* x, int64_t rows, int64_t cols, void* codes, float* scales,
+                                    hipStream_t stream);
+hipError_t launch_fp8_quantize_tensor(const void* w, int64_t rows, int64_t cols, void* codes, float* scale,
+                                      hipStream_t stream);
+hipError_t launch_fp8_gemm(const void* x_codes, const float* x_scales, const void* w_codes, const float* w_scale,
+                           void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

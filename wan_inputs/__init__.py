@@ -130,3 +130,66 @@ def sample_rows(w, n=4096):
     flat = torch.randperm(total, generator=g)[:min(n, total)]
     bh, i = flat // w.s_q, flat % w.s_q
     return torch.stack([bh // w.heads, bh % w.heads, i], dim=1)
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 GEMM of the DiT linear layers (y = x w^T).  The pages give the model width only through the
+# attention shape: 40 heads x 128 channels = 5,120 for the 14B model (12 x 128 = 1,536 for 1.3B);
+# they print no FFN width, so the workloads are the width-preserving projections (the Q, K, V and
+# output projections of a block), m = the 75,600 video tokens of one 720p, 81-frame sample.
+# Recipe: activations x [m, k] are N(0, 1) with 1% of the input-feature columns (picked without
+# replacement from a CPU generator seeded with seed + 1) multiplied by 8 -- outlier channels, the
+# reason activations get a scale per token; weights w [n, k] are N(0, 1/k).  Each is drawn from
+# its own torch.Generator on the target device (x with seed, w with seed + 2), rounded to bf16.
+
+
+@dataclass(frozen=True)
+class LinearWorkload:
+    name: str
+    m: int
+    n: int
+    k: int
+    outlier_frac: float
+    seed: int
+    description: str
+
+    @property
+    def flops(self):
+        return 2 * self.m * self.n * self.k
+
+
+LINEAR_WORKLOADS = {
+    w.name: w for w in [
+        LinearWorkload("wan14b_720p_proj_fp8", 75600, 5120, 5120, 0.01, 20250010,
+                       "Wan-14B width-preserving projection (5120 -> 5120) over the 75,600 tokens "
+                       "of a 720x1280x81 sample, FP8 e4m3 with per-token / per-tensor scales"),
+        LinearWorkload("wan1.3b_480p_proj_fp8", 32760, 1536, 1536, 0.01, 20250011,
+                       "Wan-1.3B width-preserving projection (1536 -> 1536) over the 32,760 tokens "
+                       "of a 480x832x81 sample"),
+    ]
+}
+
+
+def random_activations(m, k, seed, outlier_frac=0.01, device="cpu"):
+    """x [m, k] bfloat16: N(0, 1), round(outlier_frac * k) columns scaled by 8."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    x = torch.randn((m, k), generator=gen, dtype=torch.float32, device=device)
+    n_out = int(round(outlier_frac * k))
+    if n_out:
+        cols = torch.randperm(k, generator=torch.Generator().manual_seed(seed + 1))[:n_out]
+        x[:, cols.to(device)] *= 8.0
+    return x.to(torch.bfloat16)
+
+
+def random_weights(n, k, seed, device="cpu"):
+    """w [n, k] bfloat16: N(0, 1/k)."""
+    gen = torch.Generator(device=device).manual_seed(seed + 2)
+    w = torch.randn((n, k), generator=gen, dtype=torch.float32, device=device)
+    return w.mul_(k ** -0.5).to(torch.bfloat16)
+
+
+def make_linear(w, device="cpu"):
+    """(x [m, k], w [n, k]) bfloat16 for a linear workload (name or LinearWorkload)."""
+    if isinstance(w, str):
+        w = LINEAR_WORKLOADS[w]
+    return random_activations(w.m, w.k, w.seed, w.outlier_frac, device), random_weights(w.n, w.k, w.seed, device)
