@@ -8,8 +8,10 @@ HBM.  Prints ONE JSON line: the headline is the bf16 self-attention of the Wan-1
 counted as 4*b*heads*s_q*s_kv*head_dim; "configs" adds every other workload (480p frame,
 Wan-1.3B 480p, text cross-attention, the 8-bit path at the 720p shape) measured the same way, and
 the bf16 attention backward (dQ, dK, dV from the forward's output and row log-sum-exp) at the
-Wan-1.3B 480p and Wan-14B 720p shapes, in TFLOP/s counted as 8*b*heads*s_q*s_kv*head_dim.
-"roofline" is for the dominant kernel, "cpu_baseline" times the plain fp64 CPU oracle on a
+Wan-1.3B 480p and Wan-14B 720p shapes, in TFLOP/s counted as 8*b*heads*s_q*s_kv*head_dim, and the
+FP8 GEMM of the DiT linear layers (per-token activation quantisation + GEMM, the weights quantised
+once beforehand) at the Wan-14B and Wan-1.3B width-preserving projections, in TFLOP/s counted as
+2*m*n*k against the 5.0 PFLOP/s dense fp8 peak.  "roofline" is for the dominant kernel, "cpu_baseline" times the plain fp64 CPU oracle on a
 bounded sample of query rows of the same workload.
 """
 
@@ -161,6 +163,34 @@ def run_backward(name, steps, warmup):
             "mfma_tflops": 3.5 * w.flops / (ms * 1e-3) / 1e12}
 
 
+def run_linear(name, steps, warmup):
+    """The FP8 linear at a projection shape: one step = per-token quantisation of x plus the GEMM
+    (wan_fp8_quantize_rows + wan_fp8_gemm); the weight is quantised once, before the timed region.
+    The GEMM alone is timed as well."""
+    import torch
+    import video_diffusion_transformer_wan_amd as wan
+    import wan_inputs
+    w = wan_inputs.LINEAR_WORKLOADS[name]
+    x, wt = wan_inputs.make_linear(w, device="cuda")
+    wc, ws = wan.fp8_quantize_tensor(wt)
+    xc = torch.empty((w.m, w.k), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((w.m,), dtype=torch.float32, device="cuda")
+    y = torch.empty((w.m, w.n), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        wan.wan_fp8_quantize_rows(x, w.m, w.k, xc, xs, stream)
+        wan.wan_fp8_gemm(xc, xs, wc, ws, y, w.m, w.n, w.k, stream)
+
+    ms = time_calls(step, steps, warmup, stream)
+    gemm_ms = time_calls(lambda: wan.wan_fp8_gemm(xc, xs, wc, ws, y, w.m, w.n, w.k, stream), steps, warmup, stream)
+    tf = w.flops / (ms * 1e-3) / 1e12
+    gtf = w.flops / (gemm_ms * 1e-3) / 1e12
+    return {"workload": name, "path": "fp8 linear", "m": w.m, "n": w.n, "k": w.k, "ms": ms, "tflops": tf,
+            "frac_of_peak": tf / PEAK_TFLOPS["int8_fp8"], "gemm_ms": gemm_ms, "gemm_tflops": gtf,
+            "gemm_frac_of_peak": gtf / PEAK_TFLOPS["int8_fp8"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -171,6 +201,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--backward-only", default=None, metavar="WORKLOAD",
                     help="only time the bf16 backward at this workload's shape (for profiling)")
+    ap.add_argument("--linear-only", default=None, metavar="WORKLOAD",
+                    help="only time the FP8 linear at this projection shape (for profiling)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -189,8 +221,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "dispatches": max(1, args.steps)}), flush=True)
         return
-    if args.backward_only:
-        res = run_backward(args.backward_only, args.steps, args.warmup)
+    if args.backward_only or args.linear_only:
+        res = (run_backward(args.backward_only, args.steps, args.warmup) if args.backward_only
+               else run_linear(args.linear_only, args.steps, args.warmup))
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}), flush=True)
         return
     import video_diffusion_transformer_wan_amd as wan
@@ -234,6 +267,13 @@ def main():
             except Exception as e:
                 res = {"workload": name, "error": str(e)}
             configs[name + ":backward"] = res
+            torch.cuda.empty_cache()
+        for name in wan_inputs.LINEAR_WORKLOADS:
+            try:
+                res = run_linear(name, args.steps, args.warmup)
+            except Exception as e:
+                res = {"workload": name, "error": str(e)}
+            configs[name] = res
             torch.cuda.empty_cache()
 
     line = {

@@ -17,11 +17,14 @@
 //    accumulators hold one token and 4 consecutive features per group: the epilogue scales them
 //    by scale_x[token] * scale_w and stores 4 bf16 at a time.  Wave (wm, wn) computes tokens
 //    64 wm .. +63 and features 128 wn .. +127 (4 x 2 accumulators of 32 x 32).  W~ and X~ tiles of
-//    64 K bytes stream from HBM straight into a 4-stage LDS ring (buffer_load ... lds), three
-//    stages ahead, rows past M or N reading as zeros; 16-byte chunk c of tile row r sits at chunk
+//    64 K bytes stream from HBM straight into a 5-stage LDS ring (buffer_load ... lds), four
+//    stages ahead, rows past M or N reading as zeros; each step's operands are read into
+//    registers during the step before (two register sets); 16-byte chunk c of tile row r sits at chunk
 //    c ^ sigma(r), sigma(r) = ((r >> 1) ^ (r >> 2)) & 3, so that the operand reads (16 rows, one
 //    chunk, per 16 lanes; or 8 rows per 8 lanes) hit distinct banks.  Workgroups are numbered so
 //    that the 32 CUs of one XCD share 4 token tiles and 8 feature tiles in their L2.
+
+#include <type_traits>
 
 #include "wan_attn_internal.h"
 
@@ -138,7 +141,7 @@ constexpr int kTN = 256;                 // features per workgroup tile
 constexpr int kTK = 64;                  // K bytes per stage (one MFMA step)
 constexpr int kTileBytes = 256 * kTK;    // 16 KB per operand tile
 constexpr int kStage = 2 * kTileBytes;   // [W | X]
-constexpr int kStages = 4;
+constexpr int kStages = 5;               // 160 KB of LDS
 constexpr int kLoadsPerStage = 4;        // direct-to-LDS loads per wave per stage
 constexpr int kGroupM = 4;               // token tiles per group of consecutive work items
 
@@ -162,11 +165,12 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
   return r;
 }
 
-// Direct global -> LDS load of 16 bytes per lane to lds_addr + 16 * lane (bytes past the buffer's
-// end read as zeros).  Inline asm: the compiler would otherwise wait for each of these loads
-// before the next LDS read; the kernel waits for them itself (s_waitcnt vmcnt, counted).
-__device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
-  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
+// Direct global -> LDS load of 16 bytes per lane to lds_addr + 16 * lane from byte voff + soff of
+// the buffer (rows past the buffer's end read as zeros).  Inline asm: the compiler would otherwise
+// wait for each of these loads before the next LDS read; the kernel waits for them itself
+// (s_waitcnt vmcnt, counted).
+__device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff, unsigned soff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, %3 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr), "s"(soff));
 }
 
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
@@ -197,12 +201,10 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
 
   // loads: wave wv writes 1 KB blocks 2wv, 2wv+1 of each 16 KB tile (16 rows of 64 bytes per
   // block); lane i fetches the logical chunk that belongs at physical chunk i % 4 of its row
-  const uint8_t* wbase = p.w + n0 * K;
-  const uint8_t* xbase = p.x + m0 * K;
-  // bytes from a stage's base (the tile's first row, K offset koff) to the end of its last valid
-  // row: valid rows * K - koff; rows past m or n read as zeros
-  const int64_t wbytes = min((int64_t)kTN, p.n - n0) * K;
-  const int64_t xbytes = min((int64_t)kTM, p.m - m0) * K;
+  // one descriptor per operand tile, over its valid rows (rows past m or n read as zeros: their
+  // offset row * K + chunk is past valid rows * K); the K position of a stage is the scalar offset
+  const u32x4_t wr = rsrc_words(p.w + n0 * K, min((int64_t)kTN, p.n - n0) * K);
+  const u32x4_t xr = rsrc_words(p.x + m0 * K, min((int64_t)kTM, p.m - m0) * K);
   unsigned src_off[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
@@ -211,19 +213,18 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
   }
   const int n_k = K / kTK;
   auto issue = [&](int kk) __attribute__((always_inline)) {
-    const int64_t koff = (int64_t)kk * kTK;
-    const u32x4_t wr = rsrc_words(wbase + koff, wbytes - koff);
-    const u32x4_t xr = rsrc_words(xbase + koff, xbytes - koff);
+    const unsigned koff = (unsigned)(kk * kTK);
     const unsigned st = lds + (unsigned)((kk % kStages) * kStage);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      dma_b128(wr, st + 1024 * (2 * wv + it), src_off[it]);
-      dma_b128(xr, st + kTileBytes + 1024 * (2 * wv + it), src_off[it]);
+      dma_b128(wr, st + 1024 * (2 * wv + it), src_off[it], koff);
+      dma_b128(xr, st + kTileBytes + 1024 * (2 * wv + it), src_off[it], koff);
     }
   };
   // wait until the stage issued before the last `after` stages has landed
   auto wait_stage = [&](int after) __attribute__((always_inline)) {
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerStage));
+    if (after >= 3) __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kLoadsPerStage));
+    else if (after == 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerStage));
     else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerStage);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
@@ -258,24 +259,49 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fi][ti][r] = 0.0f;
 
-  issue(0);
-  if (n_k > 1) issue(1);
-  if (n_k > 2) issue(2);
-  for (int kk = 0; kk < n_k; ++kk) {
-    wait_stage(min(n_k - 1 - kk, 2));
-    barrier();   // stage kk has landed everywhere; every wave is done with stage kk - 1
-    if (kk + 3 < n_k) issue(kk + 3);
+  // Pipeline: stage s is loaded at step s - 4 (into the slot of stage s - 5, whose operands every
+  // wave read during step s - 6 and fed to its MFMAs during step s - 5), waited for at step s - 1,
+  // when its operands are read into registers, and multiplied at step s.  The barrier of step kk
+  // comes after every wave's MFMAs of step kk - 1.
+  i32x8_t aop[2][4], bop[2][2];
+  auto read_ops = [&](int kk, int buf) __attribute__((always_inline)) {
     const unsigned char* st = smem + (kk % kStages) * kStage;
-    i32x8_t bop[2];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) bop[ti] = read8(st, boff[ti]);
+    for (int ti = 0; ti < 2; ++ti) bop[buf][ti] = read8(st, boff[ti]);
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi) {
-      const i32x8_t aop = read8(st, aoff[fi]);
+    for (int fi = 0; fi < 4; ++fi) aop[buf][fi] = read8(st, aoff[fi]);
+  };
+  for (int s0 = 0; s0 < 4; ++s0)
+    if (s0 < n_k) issue(s0);
+  wait_stage(min(n_k - 1, 3));
+  barrier();
+  read_ops(0, 0);
+  // one step; the register set is a compile-time index (the loop runs two steps per iteration)
+  auto step = [&](int kk, auto cur_tag) __attribute__((always_inline)) {
+    constexpr int cur = decltype(cur_tag)::value;
+    if (kk + 1 < n_k) wait_stage(min(n_k - 2 - kk, 2));
+    barrier();   // stage kk+1 has landed everywhere; every wave is done with step kk-1
+    if (kk + 4 < n_k) issue(kk + 4);
+    // (on the last step this reads a stale slot whose values go unused: no branch around the reads)
+    read_ops(kk + 1, cur ^ 1);
+#pragma unroll
+    for (int fi = 0; fi < 4; ++fi)
 #pragma unroll
       for (int ti = 0; ti < 2; ++ti)
-        acc[fi][ti] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop, bop[ti], acc[fi][ti], 0, 0, 0, 0, 0, 0);
+        acc[fi][ti] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(aop[cur][fi], bop[cur][ti], acc[fi][ti], 0, 0,
+                                                                       0, 0, 0, 0);
+    // the next step's 12 operand reads spread between these 8 MFMAs (one MFMA, two reads), not
+    // issued as one burst that fills the LDS queue while the matrix core waits for this wave
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  };
+  for (int kk = 0; kk < n_k; kk += 2) {
+    step(kk, std::integral_constant<int, 0>{});
+    if (kk + 1 < n_k) step(kk + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: lane owns token m0 + 64 wm + 32 ti + l32 and features n0 + 128 wn + 32 fi + 8 g + 4 h .. +3
