@@ -26,6 +26,9 @@ Modules:
   fp8_gemm  -- the FP8 GEMM of the DiT linear layers (per-token activation and per-tensor weight
                e4m3fn quantisation, exact product): "Wan模型是什么它能做什么" explainer,
                section 4.2.
+  block_sparse -- block-sparse attention in the style of Video Sparse Attention: 64-token block
+               means, block scores, top-k key blocks per query block, exact attention over the
+               selected keys (the FastWan / VSA article, sections on VSA and its kernel).
 
 Who may use it: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py``.  The product path (the HIP library and its Python binding) never imports, links or
