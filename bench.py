@@ -11,7 +11,9 @@ the bf16 attention backward (dQ, dK, dV from the forward's output and row log-su
 Wan-1.3B 480p and Wan-14B 720p shapes, in TFLOP/s counted as 8*b*heads*s_q*s_kv*head_dim, and the
 FP8 GEMM of the DiT linear layers (per-token activation quantisation + GEMM, the weights quantised
 once beforehand) at the Wan-14B and Wan-1.3B width-preserving projections, in TFLOP/s counted as
-2*m*n*k against the 5.0 PFLOP/s dense fp8 peak.  "roofline" is for the dominant kernel, "cpu_baseline" times the plain fp64 CPU oracle on a
+2*m*n*k against the 5.0 PFLOP/s dense fp8 peak, and the block-sparse (VSA-style) attention at the
+Wan-1.3B 16x28x52 and Wan-14B 720p shapes (87.5% of the 64-token key blocks dropped), in TFLOP/s of
+the attended keys, with its speed-up over the dense forward at the same shape.  "roofline" is for the dominant kernel, "cpu_baseline" times the plain fp64 CPU oracle on a
 bounded sample of query rows of the same workload.
 """
 
@@ -191,6 +193,52 @@ def run_linear(name, steps, warmup):
             "gemm_frac_of_peak": gtf / PEAK_TFLOPS["int8_fp8"]}
 
 
+def run_vsa(name, steps, warmup):
+    """Block-sparse (VSA-style) attention at a Wan shape: one step = the coarse stage (block means,
+    scores, top-keep selection) plus the fine block-sparse attention (wan_vsa_select + wan_vsa_attn).
+    The fine stage alone, the coarse stage alone and the dense bf16 forward at the same shape are
+    timed as well.  TFLOP/s count 4 * d * (query rows x attended keys) of the selection made."""
+    import torch
+    import video_diffusion_transformer_wan_amd as wan
+    import wan_inputs
+    w = wan_inputs.VSA_WORKLOADS[name]
+    q, k, v = wan_inputs.make_vsa(w, device="cuda")
+    b, H, s = w.batch, w.heads, w.s
+    n_qb = -(-s // 64)
+    idx = torch.empty((b, H, n_qb, w.keep), dtype=torch.int32, device="cuda")
+    scratch = torch.empty(wan.wan_vsa_select_scratch_bytes(b, H, s, s) // 4, dtype=torch.float32, device="cuda")
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    d = wan_inputs.HEAD_DIM
+
+    def coarse():
+        wan.wan_vsa_select(q, k, b, H, s, s, d, w.keep, idx, scratch, stream)
+
+    def fine():
+        wan.wan_vsa_attn(q, k, v, idx, o, b, H, s, s, d, w.keep, stream)
+
+    def both():
+        coarse()
+        fine()
+
+    ms = time_calls(both, steps, warmup, stream)
+    fine_ms = time_calls(fine, steps, warmup, stream)
+    coarse_ms = time_calls(coarse, steps, warmup, stream)
+    dense_ms = time_calls(lambda: wan.wan_attn_fwd(q, k, v, o, b, H, s, s, d, wan.WAN_ATTN_BF16, stream),
+                          max(2, steps // 2), 1, stream)
+    both()
+    keys = torch.clamp(s - 64 * idx.long(), max=64).sum(dim=-1)                  # [b, H, n_qb]
+    rows = torch.clamp(s - 64 * torch.arange(n_qb, device="cuda"), max=64)      # [n_qb]
+    flops = float(4 * d * (keys * rows).sum().item())
+    tf = flops / (ms * 1e-3) / 1e12
+    ftf = flops / (fine_ms * 1e-3) / 1e12
+    return {"workload": name, "path": "vsa block-sparse bf16", "batch": b, "heads": H, "s": s, "keep": w.keep,
+            "sparsity": 1.0 - w.keep / -(-s // 64), "ms": ms, "tflops": tf, "fine_ms": fine_ms,
+            "fine_tflops": ftf, "fine_frac_of_peak": ftf / PEAK_TFLOPS["bf16"], "coarse_ms": coarse_ms,
+            "dense_ms": dense_ms, "speedup_vs_dense": dense_ms / ms, "fine_speedup_vs_dense": dense_ms / fine_ms,
+            "flops": flops}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,6 +251,8 @@ def main():
                     help="only time the bf16 backward at this workload's shape (for profiling)")
     ap.add_argument("--linear-only", default=None, metavar="WORKLOAD",
                     help="only time the FP8 linear at this projection shape (for profiling)")
+    ap.add_argument("--vsa-only", default=None, metavar="WORKLOAD",
+                    help="only time the block-sparse attention at this shape (for profiling)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -221,9 +271,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "dispatches": max(1, args.steps)}), flush=True)
         return
-    if args.backward_only or args.linear_only:
+    if args.backward_only or args.linear_only or args.vsa_only:
         res = (run_backward(args.backward_only, args.steps, args.warmup) if args.backward_only
-               else run_linear(args.linear_only, args.steps, args.warmup))
+               else run_linear(args.linear_only, args.steps, args.warmup) if args.linear_only
+               else run_vsa(args.vsa_only, args.steps, args.warmup))
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res.items()}), flush=True)
         return
     import video_diffusion_transformer_wan_amd as wan
@@ -271,6 +322,13 @@ def main():
         for name in wan_inputs.LINEAR_WORKLOADS:
             try:
                 res = run_linear(name, args.steps, args.warmup)
+            except Exception as e:
+                res = {"workload": name, "error": str(e)}
+            configs[name] = res
+            torch.cuda.empty_cache()
+        for name in wan_inputs.VSA_WORKLOADS:
+            try:
+                res = run_vsa(name, args.steps, args.warmup)
             except Exception as e:
                 res = {"workload": name, "error": str(e)}
             configs[name] = res

@@ -1,6 +1,7 @@
 /*
  * wan_attn.h -- C ABI of the MI355X (gfx950) attention forward for Wan video DiT blocks (and of the
- * attention backward and the FP8 GEMM of the DiT linear layers, declared further below).
+ * attention backward, the FP8 GEMM of the DiT linear layers and block-sparse attention, declared
+ * further below).
  *
  * Operation (every entry point below computes it, or a stage of it):
  *   O[b, i, h, :] = sum_j softmax_j( Q[b,i,h,:] . K[b,j,h,:] / sqrt(head_dim) ) * V[b, j, h, :]
@@ -55,7 +56,7 @@ enum wan_attn_status {
   WAN_ATTN_EALIGN = -2,        /* a pointer is not 16-byte aligned                            */
   WAN_ATTN_ENOMEM = -3,        /* scratch allocation failed                                   */
   WAN_ATTN_ELAUNCH = -4,       /* the HIP runtime refused a launch or a query                 */
-  WAN_ATTN_EUNSUPPORTED = -5   /* head_dim other than 128; an FP8 GEMM size outside its limits */
+  WAN_ATTN_EUNSUPPORTED = -5   /* head_dim other than 128; an FP8 GEMM or VSA size outside its limits */
 };
 
 /*
@@ -168,6 +169,44 @@ int wan_fp8_quantize_tensor(const void* w, int64_t rows, int64_t cols, void* cod
 /* y [m, n] bf16 = (x_codes [m, k] . w_codes [n, k]^T) * x_scales[m] * (*w_scale), as above. */
 int wan_fp8_gemm(const void* x_codes, const void* x_scales, const void* w_codes, const void* w_scale,
                  void* y, int64_t m, int64_t n, int64_t k, void* stream);
+
+/*
+ * Block-sparse attention in the style of Video Sparse Attention (VSA) (the FastWan / VSA article,
+ * sections "传统稀疏注意力，为何会在蒸馏中失效？" and "一张卡，秒生视频": a coarse stage picks the key
+ * blocks that matter, a fine stage runs block-sparse attention over them; 64 x 64 blocks; 87.5%
+ * sparsity).  Blocks are 64 consecutive tokens of the flattened sequence from token 0 (the last one
+ * may be partial); n_qb = ceil(s_q/64), n_kb = ceil(s_kv/64).
+ *   Coarse: per (batch, head), mean_q[i] and mean_k[j] = the fp32 means of Q and K over the real
+ *   tokens of each block; score[i, j] = mean_q[i] . mean_k[j] / sqrt(128) in fp32; for every query
+ *   block i the `keep` key blocks of largest score (equal scores: lower index first), listed in
+ *   ascending order: block_idx [batch, heads, n_qb, keep] int32.
+ *   Fine: O[b, t, h, :] = sum over the keys of the selected blocks of query block t/64 of
+ *   softmax(Q . K / sqrt(128)) V, the softmax over those keys alone; bf16 products on the MFMA,
+ *   fp32 accumulation and softmax, bf16 output.
+ * q, k, v, o as in the header comment (bf16, 16-byte aligned; o must not overlap q, k or v).
+ * keep: 1 <= keep <= n_kb (WAN_ATTN_EINVAL otherwise); n_kb <= 8192 (WAN_ATTN_EUNSUPPORTED).
+ */
+
+/* Bytes of scratch wan_vsa_select needs: the block means, (n_qb + n_kb) * batch * heads * 512. */
+size_t wan_vsa_select_scratch_bytes(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv);
+
+/* Coarse stage: block_idx [batch, heads, n_qb, keep] int32 (device memory, 16-byte aligned, owned by
+ * the caller), from q and k.  scratch: wan_vsa_select_scratch_bytes(...) bytes, 16-byte aligned, not
+ * overlapping any other argument; it holds the block means after the call. */
+int wan_vsa_select(const void* q, const void* k, int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                   int64_t head_dim, int64_t keep, void* block_idx, void* scratch, void* stream);
+
+/* Fine stage for a given block list block_idx [batch, heads, n_qb, keep] int32 (any indices: an entry
+ * outside [0, n_kb) is skipped, a repeated one counts twice; the rows of a query block whose list has
+ * no valid entry are undefined).  No scratch memory. */
+int wan_vsa_attn(const void* q, const void* k, const void* v, const void* block_idx, void* o,
+                 int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim, int64_t keep,
+                 void* stream);
+
+/* Both stages.  keep <= 0 selects ceil(n_kb / 8) (87.5% sparsity).  The block list and the block means
+ * live in scratch allocated and freed on `stream` (WAN_ATTN_ENOMEM if that fails). */
+int wan_vsa_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t heads,
+                int64_t s_q, int64_t s_kv, int64_t head_dim, int64_t keep, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* wan_attn_strerror(int code);

@@ -178,3 +178,59 @@ def test_fp8_quantize_argument_checks(fn, kw, code):
 ])
 def test_fp8_gemm_argument_checks(kw, code):
     assert _fp8("gemm", **kw) == code
+
+
+def _vsa(fn, **kw):
+    """The block-sparse entry points with far-apart fake device addresses (every case fails a check
+    before the first HIP call)."""
+    lib = ensure_built()
+    a = dict(q=1 << 24, k=1 << 25, v=1 << 26, idx=1 << 27, o=1 << 28, scratch=1 << 29,
+             b=1, H=1, sq=64, skv=512, d=128, keep=1)
+    a.update(kw)
+    if fn == "select":
+        return lib.wan_vsa_select(a["q"], a["k"], a["b"], a["H"], a["sq"], a["skv"], a["d"], a["keep"], a["idx"],
+                                  a["scratch"], None)
+    if fn == "attn":
+        return lib.wan_vsa_attn(a["q"], a["k"], a["v"], a["idx"], a["o"], a["b"], a["H"], a["sq"], a["skv"], a["d"],
+                                a["keep"], None)
+    return lib.wan_vsa_fwd(a["q"], a["k"], a["v"], a["o"], a["b"], a["H"], a["sq"], a["skv"], a["d"], a["keep"], None)
+
+
+@pytest.mark.parametrize("fn", ["select", "attn", "fwd"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), wan.WAN_ATTN_EINVAL),
+    (dict(k=None), wan.WAN_ATTN_EINVAL),
+    (dict(b=0), wan.WAN_ATTN_EINVAL),
+    (dict(skv=0), wan.WAN_ATTN_EINVAL),
+    (dict(d=64), wan.WAN_ATTN_EUNSUPPORTED),
+    (dict(keep=9), wan.WAN_ATTN_EINVAL),                      # more than the 8 key blocks
+    (dict(skv=8192 * 64 + 1), wan.WAN_ATTN_EUNSUPPORTED),     # beyond the selection sort's capacity
+    (dict(q=(1 << 24) + 8), wan.WAN_ATTN_EALIGN),
+    (dict(b=1 << 20, H=4096), wan.WAN_ATTN_EINVAL),           # coarse-stage grid beyond 31 bits
+])
+def test_vsa_argument_checks(fn, kw, code):
+    assert _vsa(fn, **kw) == code
+
+
+@pytest.mark.parametrize("fn,kw,code", [
+    ("select", dict(keep=0), wan.WAN_ATTN_EINVAL),
+    ("attn", dict(keep=0), wan.WAN_ATTN_EINVAL),
+    ("select", dict(idx=None), wan.WAN_ATTN_EINVAL),
+    ("select", dict(scratch=None), wan.WAN_ATTN_EINVAL),
+    ("select", dict(idx=(1 << 27) + 4), wan.WAN_ATTN_EALIGN),
+    ("select", dict(idx=1 << 24), wan.WAN_ATTN_EINVAL),       # block list overlaps q
+    ("select", dict(scratch=(1 << 25) + 16), wan.WAN_ATTN_EINVAL),   # scratch overlaps k
+    ("attn", dict(idx=None), wan.WAN_ATTN_EINVAL),
+    ("attn", dict(v=None), wan.WAN_ATTN_EINVAL),
+    ("attn", dict(o=1 << 26), wan.WAN_ATTN_EINVAL),            # o overlaps v
+    ("attn", dict(o=(1 << 27) - 64), wan.WAN_ATTN_EINVAL),     # o overlaps the block list
+    ("fwd", dict(o=None), wan.WAN_ATTN_EINVAL),
+])
+def test_vsa_more_argument_checks(fn, kw, code):
+    assert _vsa(fn, **kw) == code
+
+
+def test_vsa_scratch_bytes():
+    ensure_built()
+    assert wan.wan_vsa_select_scratch_bytes(2, 3, 150, 700) == 2 * 3 * (3 + 11) * 512
+    assert wan.wan_vsa_select_scratch_bytes(0, 3, 150, 700) == 0

@@ -52,6 +52,10 @@ _SIGNATURES = {
     "wan_fp8_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "wan_fp8_quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "wan_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "wan_vsa_select_scratch_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64]),
+    "wan_vsa_select": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
+    "wan_vsa_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_vsa_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_attn_version": (ctypes.c_int, []),
 }
@@ -286,3 +290,75 @@ def fp8_linear(x, w_codes, w_scale, out=None, stream=None):
     """y = x w^T in FP8 for x [m, k] bf16 and a weight quantised once with fp8_quantize_tensor."""
     xc, xs = fp8_quantize_rows(x, stream)
     return fp8_gemm(xc, xs, w_codes, w_scale, out, stream)
+
+
+VSA_BLOCK = 64
+
+
+def vsa_default_keep(s_kv):
+    """ceil(n_kb / 8) key blocks of 64 tokens: 87.5% sparsity."""
+    return max(1, -(-(-(-s_kv // VSA_BLOCK)) // 8))
+
+
+def wan_vsa_select_scratch_bytes(batch, heads, s_q, s_kv):
+    return lib().wan_vsa_select_scratch_bytes(batch, heads, s_q, s_kv)
+
+
+def wan_vsa_select(q, k, batch, heads, s_q, s_kv, head_dim, keep, block_idx, scratch, stream=None):
+    rc = lib().wan_vsa_select(_ptr(q), _ptr(k), batch, heads, s_q, s_kv, head_dim, keep, _ptr(block_idx),
+                              _ptr(scratch), _stream(stream))
+    _check(rc, "wan_vsa_select")
+
+
+def wan_vsa_attn(q, k, v, block_idx, o, batch, heads, s_q, s_kv, head_dim, keep, stream=None):
+    rc = lib().wan_vsa_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(o), batch, heads, s_q, s_kv, head_dim,
+                            keep, _stream(stream))
+    _check(rc, "wan_vsa_attn")
+
+
+def wan_vsa_fwd(q, k, v, o, batch, heads, s_q, s_kv, head_dim, keep, stream=None):
+    rc = lib().wan_vsa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, s_q, s_kv, head_dim, keep,
+                           _stream(stream))
+    _check(rc, "wan_vsa_fwd")
+
+
+def vsa_select(q, k, keep=None, stream=None):
+    """Coarse stage of block-sparse attention: the `keep` key blocks (64 tokens) of largest block score
+    for every query block, block_idx [b, H, ceil(s_q/64), keep] int32 in ascending order."""
+    import torch
+    b, s_q, H, d = q.shape
+    if k.dtype != torch.bfloat16 or not k.is_cuda or not k.is_contiguous() or k.dim() != 4 or k.shape[0] != b or k.shape[2] != H:
+        raise ValueError("k must be a contiguous bfloat16 tensor [b, s_kv, H, d] matching q")
+    if q.dtype != torch.bfloat16 or not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous 4-d bfloat16 CUDA tensor [b, s, H, d]")
+    s_kv = k.shape[1]
+    keep = vsa_default_keep(s_kv) if keep is None else keep
+    idx = torch.empty((b, H, -(-s_q // VSA_BLOCK), keep), dtype=torch.int32, device=q.device)
+    scratch = torch.empty(max(wan_vsa_select_scratch_bytes(b, H, s_q, s_kv), 16) // 4, dtype=torch.float32,
+                          device=q.device)
+    wan_vsa_select(q, k, b, H, s_q, s_kv, d, keep, idx, scratch, stream)
+    return idx
+
+
+def vsa_attention(q, k, v, block_idx, out=None, stream=None):
+    """Fine stage: attention of every query block over the keys of its listed key blocks
+    (block_idx [b, H, ceil(s_q/64), keep] int32); returns o [b, s_q, H, 128] bfloat16."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    if (block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4
+            or tuple(block_idx.shape[:3]) != (b, H, -(-s_q // VSA_BLOCK))):
+        raise ValueError("block_idx must be a contiguous int32 tensor [b, H, ceil(s_q/64), keep]")
+    if out is None:
+        out = torch.empty_like(q)
+    wan_vsa_attn(q, k, v, block_idx, out, b, H, s_q, s_kv, d, block_idx.shape[3], stream)
+    return out
+
+
+def vsa_forward(q, k, v, keep=None, out=None, stream=None):
+    """Both stages in one call (the block list in library scratch); keep None: ceil(n_kb / 8)."""
+    import torch
+    b, H, s_q, s_kv, d = _check_tensors(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    wan_vsa_fwd(q, k, v, out, b, H, s_q, s_kv, d, 0 if keep is None else keep, stream)
+    return out

@@ -163,6 +163,16 @@ int check_fp8_dims(int64_t rows, int64_t cols) {
 
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
+// VSA sizes: the key-block count within the selection sort's LDS, keep within [1, n_kb], and the
+// coarse stage's one-dimensional grids (2 * batch * heads * blocks workgroups) within 31 bits.
+int check_vsa(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t keep) {
+  const int64_t n_qb = wan::ceil_div(s_q, 64), n_kb = wan::ceil_div(s_kv, 64);
+  if (n_kb > wan::vsa_max_key_blocks()) return WAN_ATTN_EUNSUPPORTED;
+  if (keep < 1 || keep > n_kb) return WAN_ATTN_EINVAL;
+  if ((long double)2 * batch * heads * (n_qb > n_kb ? n_qb : n_kb) > 2147483000.0L) return WAN_ATTN_EINVAL;
+  return WAN_ATTN_OK;
+}
+
 }  // namespace
 
 
@@ -177,7 +187,7 @@ const char* wan_attn_strerror(int code) {
     case WAN_ATTN_EALIGN: return "pointer not 16-byte aligned";
     case WAN_ATTN_ENOMEM: return "out of device memory for scratch";
     case WAN_ATTN_ELAUNCH: return "HIP runtime error while launching";
-    case WAN_ATTN_EUNSUPPORTED: return "unsupported size (head_dim other than 128, or an FP8 GEMM size outside its limits)";
+    case WAN_ATTN_EUNSUPPORTED: return "unsupported size (head_dim other than 128, or an FP8 GEMM or VSA size outside its limits)";
     default: return "unknown status code";
   }
 }
@@ -373,6 +383,79 @@ int wan_fp8_gemm(const void* x_codes, const void* x_scales, const void* w_codes,
                                        static_cast<const float*>(w_scale), y, m, n, k,
                                        static_cast<hipStream_t>(stream)),
                   "fp8 gemm launch");
+}
+
+size_t wan_vsa_select_scratch_bytes(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv) {
+  if (check_shape(batch, heads, s_q, s_kv, wan::kHeadDim)) return 0;
+  return wan::vsa_select_scratch_bytes(wan::AttnShape{batch, heads, s_q, s_kv});
+}
+
+int wan_vsa_select(const void* q, const void* k, int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
+                   int64_t head_dim, int64_t keep, void* block_idx, void* scratch, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  rc = check_vsa(batch, heads, s_q, s_kv, keep);
+  if (rc) return rc;
+  if (!q || !k || !block_idx || !scratch) return WAN_ATTN_EINVAL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(block_idx) || !aligned16(scratch)) return WAN_ATTN_EALIGN;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2, kb = batch * s_kv * heads * wan::kHeadDim * 2;
+  const int64_t ib = batch * heads * wan::ceil_div(s_q, 64) * keep * 4;
+  const int64_t sb = (int64_t)wan::vsa_select_scratch_bytes(sh);
+  if (overlaps(block_idx, ib, q, qb) || overlaps(block_idx, ib, k, kb) || overlaps(block_idx, ib, scratch, sb) ||
+      overlaps(scratch, sb, q, qb) || overlaps(scratch, sb, k, kb))
+    return WAN_ATTN_EINVAL;
+  WAN_LOG("vsa_select b=%lld H=%lld s_q=%lld s_kv=%lld keep=%lld", (long long)batch, (long long)heads,
+          (long long)s_q, (long long)s_kv, (long long)keep);
+  return from_hip(wan::launch_vsa_select(q, k, sh, (int)keep, static_cast<int*>(block_idx), scratch,
+                                         static_cast<hipStream_t>(stream)),
+                  "vsa select launch");
+}
+
+int wan_vsa_attn(const void* q, const void* k, const void* v, const void* block_idx, void* o, int64_t batch,
+                 int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim, int64_t keep, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  rc = check_vsa(batch, heads, s_q, s_kv, keep);
+  if (rc) return rc;
+  rc = check_qkvo(q, k, v, o, batch, heads, s_q, s_kv);
+  if (rc) return rc;
+  if (!block_idx) return WAN_ATTN_EINVAL;
+  if (!aligned16(block_idx)) return WAN_ATTN_EALIGN;
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
+  const int64_t ib = batch * heads * wan::ceil_div(s_q, 64) * keep * 4;
+  if (overlaps(o, qb, block_idx, ib)) return WAN_ATTN_EINVAL;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  WAN_LOG("vsa_attn b=%lld H=%lld s_q=%lld s_kv=%lld keep=%lld", (long long)batch, (long long)heads,
+          (long long)s_q, (long long)s_kv, (long long)keep);
+  return from_hip(wan::launch_vsa_attn(q, k, v, static_cast<const int*>(block_idx), (int)keep, o, sh,
+                                       static_cast<hipStream_t>(stream)),
+                  "vsa attention launch");
+}
+
+int wan_vsa_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t heads, int64_t s_q,
+                int64_t s_kv, int64_t head_dim, int64_t keep, void* stream) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  if (keep <= 0) keep = (wan::ceil_div(s_kv, 64) + 7) / 8;
+  rc = check_vsa(batch, heads, s_q, s_kv, keep);
+  if (rc) return rc;
+  rc = check_qkvo(q, k, v, o, batch, heads, s_q, s_kv);
+  if (rc) return rc;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const size_t idx_bytes = align256((size_t)(batch * heads * wan::ceil_div(s_q, 64) * keep) * 4);
+  void* ws = scratch_alloc(idx_bytes + wan::vsa_select_scratch_bytes(sh), st, &rc);
+  if (!ws) return rc;
+  int* idx = static_cast<int*>(ws);
+  WAN_LOG("vsa_fwd b=%lld H=%lld s_q=%lld s_kv=%lld keep=%lld", (long long)batch, (long long)heads,
+          (long long)s_q, (long long)s_kv, (long long)keep);
+  rc = from_hip(wan::launch_vsa_select(q, k, sh, (int)keep, idx, static_cast<unsigned char*>(ws) + idx_bytes, st),
+                "vsa select launch");
+  if (!rc) rc = from_hip(wan::launch_vsa_attn(q, k, v, idx, (int)keep, o, sh, st), "vsa attention launch");
+  hipError_t fe = hipFreeAsync(ws, st);
+  if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
+  return rc;
 }
 
 }  // extern "C"

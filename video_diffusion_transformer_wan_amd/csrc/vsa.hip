@@ -1,0 +1,461 @@
+// Block-sparse attention in the style of Video Sparse Attention (VSA) for gfx950 (MI355X).  The
+// FastWan / VSA article describes a coarse stage that finds the key blocks that matter and a fine
+// block-sparse attention over them, with 64 x 64 blocks and 87.5% sparsity.  Blocks here are 64
+// consecutive tokens; the coarse stage keeps, for every query block, the `keep` key blocks with
+// the largest mean_q . mean_k / sqrt(128) (ties to the lower index); the fine stage is exact
+// softmax attention over the selected keys only.
+//
+// Kernels:
+//  * vsa_pool_kernel -- one wave per (batch*head, block, tensor): the fp32 mean of Q or K over the
+//    block's real tokens (lane holds 2 channels; tokens summed in order), [bh][block][128].
+//  * vsa_select_kernel -- one workgroup per (batch*head, query block): the block scores against all
+//    key blocks in fp32 (channels summed in order), a bitonic sort of (score, index) pairs in LDS
+//    (larger score first, then lower index), then the top `keep` indices sorted ascending.
+//  * vsa_attn_kernel -- one workgroup = 4 waves = 2 query blocks (a wave pair each, 32 query rows
+//    per wave); each pair streams the K and V tiles of its selected key blocks through its own
+//    2-stage LDS ring (direct-to-LDS loads), with the bf16 forward's transposed products, LDS
+//    layouts and swizzles (S^T = K Q^T; O^T += V^T P^T by transposing V reads) and an online
+//    softmax with a running row max (the O accumulators rescaled only when some row's max grows).
+
+#include "wan_attn_internal.h"
+
+namespace wan {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kBlock = 64;
+constexpr float kNeg = -1.0e30f;
+constexpr float kScaleLog2 = 0.12751743082459868f;   // log2(e) / sqrt(128)
+constexpr float kInvSqrtD = 0.08838834764831845f;    // 1 / sqrt(128)
+constexpr unsigned kRsrcFlags = 0x00020000u;
+constexpr short kWaitVm0 = 0x0F70;
+
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+__device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(unsigned, r);
+}
+
+__device__ __forceinline__ void pair_values(float x, float& a, float& b) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  a = __builtin_bit_cast(float, (unsigned)r[0]);
+  b = __builtin_bit_cast(float, (unsigned)r[1]);
+}
+
+// Buffer resource over [base, base + bytes); loads past the end return zeros.
+__device__ __forceinline__ unsigned clamp_bytes(int64_t bytes) {
+  return bytes <= 0 ? 0u : (bytes >= 0x7fffffffLL ? 0x7fffffffu : (unsigned)bytes);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)clamp_bytes(bytes), (int)kRsrcFlags);
+}
+// The same descriptor as four words, for the inline-asm direct-to-LDS loads.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const u32x4_t r = {(unsigned)b, (unsigned)(b >> 32) & 0xFFFFu, clamp_bytes(bytes), kRsrcFlags};
+  return r;
+}
+
+__device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
+}
+
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------------
+// Coarse stage 1: block means.  Workgroup x = (batch*head * nb_max + block) * 2 + tensor (0: q,
+// 1: k); one wave (64 lanes x 2 channels).
+__global__ __launch_bounds__(64) void vsa_pool_kernel(const uint16_t* q, const uint16_t* k, int heads, int s_q,
+                                                      int s_kv, int nb_max, float* pooled_q, float* pooled_k) {
+  const int which = blockIdx.x & 1;
+  const int rest = blockIdx.x >> 1;
+  const int bh = rest / nb_max, blk = rest - bh * nb_max;
+  const int s = which == 0 ? s_q : s_kv;
+  const int nb = (s + kBlock - 1) / kBlock;
+  if (blk >= nb) return;
+  const uint16_t* x = which == 0 ? q : k;
+  float* out = which == 0 ? pooled_q : pooled_k;
+  const int b = bh / heads, h = bh - b * heads;
+  const int lane = threadIdx.x;
+  const int t0 = blk * kBlock, t1 = min(t0 + kBlock, s);
+  const int64_t stride = (int64_t)heads * kHeadDim;
+  const unsigned* src = reinterpret_cast<const unsigned*>(x + ((int64_t)b * s * heads + h) * kHeadDim) + lane;
+  float a0 = 0.0f, a1 = 0.0f;
+  for (int t = t0; t < t1; ++t) {
+    const unsigned v = src[(int64_t)t * (stride / 2)];
+    a0 += __builtin_bit_cast(float, v << 16);
+    a1 += __builtin_bit_cast(float, v & 0xffff0000u);
+  }
+  const float n = (float)(t1 - t0);
+  float* dst = out + ((int64_t)bh * nb + blk) * kHeadDim + 2 * lane;
+  dst[0] = __fdiv_rn(a0, n);
+  dst[1] = __fdiv_rn(a1, n);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Coarse stage 2: scores and top-keep selection of one query block (256 threads).  The score of
+// key block j is summed by 8 lanes, 16 consecutive channels each (in channel order), then across
+// the 8 lanes by a butterfly.  Scores and indices live in dynamic LDS, n_pow2 of each.
+constexpr int kSelThreads = 256;
+constexpr int kMaxKeyBlocks = 8192;
+
+__device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib) {
+  return sa > sb || (sa == sb && ia < ib);
+}
+
+__global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(const float* pooled_q, const float* pooled_k, int n_qb,
+                                                                 int n_kb, int n_pow2, int keep, int keep_pow2,
+                                                                 int* block_idx) {
+  extern __shared__ float sel_lds[];
+  float* score = sel_lds;
+  int* index = reinterpret_cast<int*>(sel_lds + n_pow2);
+  const int bh = blockIdx.x / n_qb, qb = blockIdx.x - bh * n_qb;
+  const int tid = threadIdx.x;
+  const int part = tid & 7;          // channels 16 part .. 16 part + 15
+  const int sub = tid >> 3;          // key block within a group of 32
+  float qm[16];
+  {
+    const float4* src = reinterpret_cast<const float4*>(pooled_q + ((int64_t)bh * n_qb + qb) * kHeadDim + 16 * part);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 x = src[i];
+      qm[4 * i] = x.x;
+      qm[4 * i + 1] = x.y;
+      qm[4 * i + 2] = x.z;
+      qm[4 * i + 3] = x.w;
+    }
+  }
+  const float* kmb = pooled_k + (int64_t)bh * n_kb * kHeadDim;
+  for (int j0 = 0; j0 < n_pow2; j0 += kSelThreads / 8) {
+    const int j = j0 + sub;
+    float acc = 0.0f;
+    if (j < n_kb) {
+      const float4* kr = reinterpret_cast<const float4*>(kmb + (int64_t)j * kHeadDim + 16 * part);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 x = kr[i];
+        acc = __builtin_fmaf(qm[4 * i], x.x, acc);
+        acc = __builtin_fmaf(qm[4 * i + 1], x.y, acc);
+        acc = __builtin_fmaf(qm[4 * i + 2], x.z, acc);
+        acc = __builtin_fmaf(qm[4 * i + 3], x.w, acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    acc += __shfl_xor(acc, 4);
+    if (part == 0 && j < n_pow2) {
+      score[j] = j < n_kb ? acc * kInvSqrtD : -__builtin_inff();   // padding sorts last
+      index[j] = j < n_kb ? j : 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  // bitonic sort, order: ranks_before (larger score first, then lower index)
+  for (int size = 2; size <= n_pow2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n_pow2; i += kSelThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;   // this half sorts in ranks_before order
+          const float si = score[i], sj = score[j];
+          const int ii = index[i], ij = index[j];
+          if (ranks_before(sj, ij, si, ii) == up) {
+            score[i] = sj;
+            score[j] = si;
+            index[i] = ij;
+            index[j] = ii;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // the first `keep` entries, sorted ascending by index (the rest of the keep_pow2 window padded)
+  for (int i = tid; i < keep_pow2; i += kSelThreads) index[i] = i < keep ? index[i] : 0x7fffffff;
+  __syncthreads();
+  for (int size = 2; size <= keep_pow2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < keep_pow2; i += kSelThreads) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const int a = index[i], c = index[j];
+          if ((c < a) == up) {
+            index[i] = c;
+            index[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  int* dst = block_idx + ((int64_t)bh * n_qb + qb) * keep;
+  for (int i = tid; i < keep; i += kSelThreads) dst[i] = index[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Fine stage.
+constexpr int kAttnWaves = 4;
+constexpr int kKBytes = kBlock * kHeadDim * 2;   // K tile, 16 KB
+constexpr int kStageBytes = 2 * kKBytes;         // [K | V]
+constexpr int kPairLds = 2 * kStageBytes;        // 2 stages per wave pair
+
+struct VsaParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int* block_idx;   // [bh][n_qb][keep]
+  uint16_t* o;
+  int heads, s_q, s_kv, n_qb, n_kb, keep, pairs_per_bh;
+};
+
+__global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPairLds];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wv >> 1, w2 = wv & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int bh = blockIdx.x / p.pairs_per_bh;
+  const int qb = 2 * (blockIdx.x - bh * p.pairs_per_bh) + pair;
+  const bool active = qb < p.n_qb;                  // wave-uniform
+  const int bb = bh / p.heads, hh = bh - bb * p.heads;
+  const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
+  unsigned char* ring = smem + pair * kPairLds;
+  const unsigned lds_ring = (unsigned)(uintptr_t)(lds_void_t*)ring;
+
+  // loads: wave w2 of the pair writes 1 KB blocks 8 w2 .. 8 w2 + 7 of the K tile and of the V tile
+  unsigned k_src[8], v_src[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int m = 8 * w2 + it;
+    const int row = 4 * m + (lane >> 4);
+    const int pch = lane & 15;
+    k_src[it] = (unsigned)(swap23(row) * stride + 16 * (pch ^ (row & 15)));
+    v_src[it] = (unsigned)(row * stride + 16 * (pch ^ ((row & 3) << 2)));
+  }
+  // operand read offsets (the bf16 forward's): K rows l32 (+32), V by transposing reads
+  const int k_rd0 = l32 * 256 + 16 * ((h ^ l32) & 1) + 32 * ((l32 >> 1) & 7);
+  int v_rd0;
+  {
+    const int g = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
+    const int x = 2 * (g & 1) + (q >> 1);
+    v_rd0 = kKBytes + (8 * (g >> 1) + kq) * 256 + 64 * kq + 16 * x + 8 * (q & 1);
+  }
+
+  const int64_t kv_head = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kv_head;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kv_head;
+  const int* list = p.block_idx + ((int64_t)bh * p.n_qb + (active ? qb : 0)) * p.keep;
+
+  // Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7 (rows past s_q read zeros)
+  const int q0 = qb * kBlock + 32 * w2;
+  bf16x8_t qf[8];
+  {
+    const unsigned char* qbase = reinterpret_cast<const unsigned char*>(p.q) +
+                                 ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2 + (int64_t)q0 * stride;
+    const __amdgpu_buffer_rsrc_t qr =
+        make_rsrc(qbase, active ? (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2 : 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      qf[c] = __builtin_bit_cast(
+          bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
+  }
+
+  auto issue = [&](int j) __attribute__((always_inline)) {
+    const int blk = list[j];
+    const bool ok = active && blk >= 0 && blk < p.n_kb;   // anything else reads as zeros
+    const int64_t off = (int64_t)(ok ? blk : 0) * kBlock * stride;
+    const int64_t bytes = ok ? (int64_t)(p.s_kv - 1 - blk * kBlock) * stride + kHeadDim * 2 : 0;
+    const u32x4_t kr = rsrc_words(kbase + off, bytes);
+    const u32x4_t vr = rsrc_words(vbase + off, bytes);
+    const unsigned st = lds_ring + (unsigned)((j & 1) * kStageBytes + 8192 * w2);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      dma_b128(kr, st + 1024 * it, k_src[it]);
+      dma_b128(vr, st + kKBytes + 1024 * it, v_src[it]);
+    }
+  };
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m = kNeg, l = 0.0f;
+
+  issue(0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  barrier();
+  for (int j = 0; j < p.keep; ++j) {
+    if (j + 1 < p.keep) issue(j + 1);
+    const int blk = list[j];
+    if (active && blk >= 0 && blk < p.n_kb) {   // an index outside [0, n_kb) is skipped
+      const unsigned char* ks = ring + (j & 1) * kStageBytes;
+      // S^T of the block: s[kb] holds keys 32 kb + swap23(8 (r / 4) + 4 h + r % 4) of the lane's row
+      f32x16_t s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int o0 = k_rd0 ^ (64 * st), o1 = k_rd0 ^ (64 * st + 32);
+        const bf16x8_t f0 = *reinterpret_cast<const bf16x8_t*>(ks + o0);
+        const bf16x8_t f1 = *reinterpret_cast<const bf16x8_t*>(ks + o0 + 8192);
+        const bf16x8_t f2 = *reinterpret_cast<const bf16x8_t*>(ks + o1);
+        const bf16x8_t f3 = *reinterpret_cast<const bf16x8_t*>(ks + o1 + 8192);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[2 * st], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[2 * st], s[1], 0, 0, 0);
+        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, qf[2 * st + 1], s[0], 0, 0, 0);
+        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, qf[2 * st + 1], s[1], 0, 0, 0);
+      }
+      // keys past s_kv (the last block only) get a score that exp2 turns into 0
+      const int kv0 = blk * kBlock;
+      if (kv0 + kBlock > p.s_kv) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (kv0 + swap23(32 * kb + 8 * (r >> 2) + 4 * h + (r & 3)) >= p.s_kv) s[kb][r] = kNeg;
+      }
+      // online softmax: the row max over both halves of the row, rescale when it grows
+      float mx = kNeg;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+      float ma, mb;
+      pair_values(mx, ma, mb);
+      const float m_new = __builtin_fmaxf(m, __builtin_fmaxf(ma, mb));
+      if (__any(m_new > m)) {
+        const float alpha = __builtin_amdgcn_exp2f((m - m_new) * kScaleLog2);
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      m = m_new;
+      const float mc = m * kScaleLog2;
+      unsigned pk[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kScaleLog2, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], kScaleLog2, -mc));
+          pk[kb][r >> 1] = cvt_pk_bf16(p0, p1);
+          l += p0 + p1;
+        }
+      // O^T += V^T P^T over the block's 4 steps of 16 keys
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int kb = t >> 1, u = t & 1;
+        const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+        const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const unsigned char* vp = ks + (v_rd0 ^ (64 * db)) + 4096 * t;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
+          const i16x4_t cat[2] = {lo, hi};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, cat), bop, o[db], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of block j+1
+    barrier();                              // block j+1 has landed; everyone is done with block j
+  }
+
+  if (active) {
+    float la, lb;
+    pair_values(l, la, lb);
+    const float inv = 1.0f / (la + lb);
+    const int row = q0 + l32;
+    if (row < p.s_q) {
+      uint16_t* dst = p.o + (((int64_t)bb * p.s_q + row) * p.heads + hh) * kHeadDim + 4 * h;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                             cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
+        }
+    }
+  }
+}
+
+int pow2_at_least(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+size_t vsa_select_scratch_bytes(const AttnShape& sh) {
+  const int64_t nq = ceil_div(sh.s_q, kBlock), nk = ceil_div(sh.s_kv, kBlock);
+  return (size_t)(sh.batch * sh.heads * (nq + nk) * kHeadDim) * sizeof(float);
+}
+
+int vsa_max_key_blocks() { return kMaxKeyBlocks; }
+
+hipError_t launch_vsa_select(const void* q, const void* k, const AttnShape& sh, int keep, int* block_idx,
+                             void* scratch, hipStream_t stream) {
+  const int n_qb = (int)ceil_div(sh.s_q, kBlock), n_kb = (int)ceil_div(sh.s_kv, kBlock);
+  const int64_t bh = sh.batch * sh.heads;
+  float* pooled_q = static_cast<float*>(scratch);
+  float* pooled_k = pooled_q + bh * n_qb * kHeadDim;
+  const int nb_max = n_qb > n_kb ? n_qb : n_kb;
+  hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)(2 * bh * nb_max)), dim3(64), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), (int)sh.heads, (int)sh.s_q,
+                     (int)sh.s_kv, nb_max, pooled_q, pooled_k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_pow2 = pow2_at_least(n_kb > 32 ? n_kb : 32);
+  const unsigned lds = (unsigned)n_pow2 * 8;
+  if (lds > 65536) return hipErrorInvalidValue;
+  if (lds > 32768) {   // above the default dynamic LDS limit of some runtimes: raise it explicitly
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(vsa_select_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)(n_qb * bh)), dim3(kSelThreads), lds, stream, pooled_q,
+                     pooled_k, n_qb, n_kb, n_pow2, keep, pow2_at_least(keep), block_idx);
+  return hipGetLastError();
+}
+
+hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, const int* block_idx, int keep, void* o,
+                           const AttnShape& sh, hipStream_t stream) {
+  VsaParams p;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.block_idx = block_idx;
+  p.o = static_cast<uint16_t*>(o);
+  p.heads = (int)sh.heads;
+  p.s_q = (int)sh.s_q;
+  p.s_kv = (int)sh.s_kv;
+  p.n_qb = (int)ceil_div(sh.s_q, kBlock);
+  p.n_kb = (int)ceil_div(sh.s_kv, kBlock);
+  p.keep = keep;
+  p.pairs_per_bh = (p.n_qb + 1) / 2;
+  const int64_t grid = sh.batch * sh.heads * p.pairs_per_bh;
+  hipLaunchKernelGGL(vsa_attn_kernel, dim3((unsigned)grid), dim3(64 * kAttnWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace wan

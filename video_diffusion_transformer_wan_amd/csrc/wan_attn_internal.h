@@ -56,6 +56,16 @@ hipError_t launch_fp8_quantize_tensor(const void* w, int64_t rows, int64_t cols,
 hipError_t launch_fp8_gemm(const void* x_codes, const float* x_scales, const void* w_codes, const float* w_scale,
                            void* y, int64_t m, int64_t n, int64_t k, hipStream_t stream);
 
+// Block-sparse (VSA-style) attention: the coarse stage (block means into `scratch`, then the
+// top-keep key blocks of every query block into block_idx [b*H][n_qb][keep] int32) and the fine
+// stage (attention over the listed key blocks).
+size_t vsa_select_scratch_bytes(const AttnShape& sh);
+int vsa_max_key_blocks();
+hipError_t launch_vsa_select(const void* q, const void* k, const AttnShape& sh, int keep, int* block_idx,
+                             void* scratch, hipStream_t stream);
+hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, const int* block_idx, int keep, void* o,
+                           const AttnShape& sh, hipStream_t stream);
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace wan

@@ -193,3 +193,46 @@ def make_linear(w, device="cpu"):
     if isinstance(w, str):
         w = LINEAR_WORKLOADS[w]
     return random_activations(w.m, w.k, w.seed, w.outlier_frac, device), random_weights(w.n, w.k, w.seed, device)
+
+
+# ---------------------------------------------------------------------------------------------
+# Block-sparse (VSA-style) attention.  The FastWan / VSA article fine-tunes Wan-1.3B with VSA on a
+# 16 x 28 x 52 video latent (taken here as the token grid: 16 latent frames of 28 x 52 tokens,
+# 23,296 tokens; the 1.3B model has 12 heads of 128) and quotes the fine kernel's speed against
+# dense attention on long sequences, so the second workload is the 720p, 81-frame 14B shape
+# (75,600 tokens, 40 heads).  Both keep ceil(n_kb / 8) of the 64-token key blocks (87.5% sparsity).
+# Q, K, V follow make_qkv's recipe (N(0, 1) in bf16, one generator seeded with the seed).
+
+
+@dataclass(frozen=True)
+class VsaWorkload:
+    name: str
+    batch: int
+    heads: int
+    s: int
+    keep: int
+    seed: int
+    description: str
+
+    @property
+    def dense_flops(self):
+        return 4 * self.batch * self.heads * self.s * self.s * HEAD_DIM
+
+
+VSA_WORKLOADS = {
+    w.name: w for w in [
+        VsaWorkload("wan1.3b_vsa_16x28x52", 1, 12, 16 * 28 * 52, 46, 20250020,
+                    "Wan-1.3B-shaped self-attention over a 16x28x52 latent token grid, keep 46 of 364 "
+                    "key blocks"),
+        VsaWorkload("wan14b_720p81f_vsa", 1, 40, 75600, 148, 20250021,
+                    "Wan-14B-shaped self-attention, 720x1280x81 frames (21x45x80 tokens), keep 148 of "
+                    "1,182 key blocks"),
+    ]
+}
+
+
+def make_vsa(w, device="cpu"):
+    """Q, K, V [b, s, H, 128] bfloat16 for a block-sparse workload (name or VsaWorkload)."""
+    if isinstance(w, str):
+        w = VSA_WORKLOADS[w]
+    return random_qkv(w.batch, w.heads, w.s, w.s, w.seed, device=device)
