@@ -184,7 +184,8 @@ int wan_fp8_gemm(const void* x_codes, const void* x_scales, const void* w_codes,
  *   softmax(Q . K / sqrt(128)) V, the softmax over those keys alone; bf16 products on the MFMA,
  *   fp32 accumulation and softmax, bf16 output.
  * q, k, v, o as in the header comment (bf16, 16-byte aligned; o must not overlap q, k or v).
- * keep: 1 <= keep <= n_kb (WAN_ATTN_EINVAL otherwise); n_kb <= 8192 (WAN_ATTN_EUNSUPPORTED).
+ * keep: 1 <= keep <= n_kb (WAN_ATTN_EINVAL otherwise); n_kb <= 4096, i.e. s_kv <= 262,144
+ * (WAN_ATTN_EUNSUPPORTED).
  */
 
 /* Bytes of scratch wan_vsa_select needs: the block means, (n_qb + n_kb) * batch * heads * 512. */

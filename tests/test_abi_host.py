@@ -204,7 +204,7 @@ def _vsa(fn, **kw):
     (dict(skv=0), wan.WAN_ATTN_EINVAL),
     (dict(d=64), wan.WAN_ATTN_EUNSUPPORTED),
     (dict(keep=9), wan.WAN_ATTN_EINVAL),                      # more than the 8 key blocks
-    (dict(skv=8192 * 64 + 1), wan.WAN_ATTN_EUNSUPPORTED),     # beyond the selection sort's capacity
+    (dict(skv=4096 * 64 + 1), wan.WAN_ATTN_EUNSUPPORTED),     # beyond the selection's LDS capacity
     (dict(q=(1 << 24) + 8), wan.WAN_ATTN_EALIGN),
     (dict(b=1 << 20, H=4096), wan.WAN_ATTN_EINVAL),           # coarse-stage grid beyond 31 bits
 ])

@@ -4,7 +4,7 @@
   float64 ones, so the GPU's list is checked to be a valid top-keep set of the oracle's scores within
   the float32 rounding of those scores (oracle.block_sparse.is_valid_selection), bound per score
   (u = 2^-24, n <= 64 tokens per block, d = 128):
-      |mean error| <= 65 u mean|x|                   (n - 1 in-order additions and the division)
+      |mean error| <= 65 u mean|x|                   (4 in-order sums of 16 tokens, their sum, the division)
       |score error| <= u (20 sum_c |mq_c mk_c| + 66 sum_c (mean|q|_c |mk_c| + |mq_c| mean|k|_c)) / sqrt(d)
   (16 in-order products per lane and a 3-level butterfly; the mean errors carried through), twice
   over for the two scores compared.  Where the scores are exact in float32 (constant blocks of small

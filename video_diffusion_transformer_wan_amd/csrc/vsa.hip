@@ -6,11 +6,11 @@
 // softmax attention over the selected keys only.
 //
 // Kernels:
-//  * vsa_pool_kernel -- one wave per (batch*head, block, tensor): the fp32 mean of Q or K over the
-//    block's real tokens (lane holds 2 channels; tokens summed in order), [bh][block][128].
-//  * vsa_select_kernel -- one workgroup per (batch*head, query block): the block scores against all
-//    key blocks in fp32 (channels summed in order), a bitonic sort of (score, index) pairs in LDS
-//    (larger score first, then lower index), then the top `keep` indices sorted ascending.
+//  * vsa_pool_kernel -- one workgroup per (batch*head, block, tensor): the fp32 mean of Q or K over
+//    the block's real tokens, [bh][block][128].
+//  * vsa_select_kernel -- one workgroup per 8 query blocks of one batch*head: their block scores
+//    against all key blocks in fp32, and per query block a radix select of the top `keep` (larger
+//    score first, then lower index), written in ascending index order.
 //  * vsa_attn_kernel -- one workgroup = 4 waves = 2 query blocks (a wave pair each, 32 query rows
 //    per wave); each pair streams the K and V tiles of its selected key blocks through its own
 //    2-stage LDS ring (direct-to-LDS loads), with the bf16 forward's transposed products, LDS
@@ -76,132 +76,187 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 
 // ---------------------------------------------------------------------------------------------
 // Coarse stage 1: block means.  Workgroup x = (batch*head * nb_max + block) * 2 + tensor (0: q,
-// 1: k); one wave (64 lanes x 2 channels).
-__global__ __launch_bounds__(64) void vsa_pool_kernel(const uint16_t* q, const uint16_t* k, int heads, int s_q,
-                                                      int s_kv, int nb_max, float* pooled_q, float* pooled_k) {
+// 1: k); 4 waves, lane = 2 channels, wave w sums tokens 16w .. 16w+15 of the block in order, and
+// the four partial sums are added in wave order.
+__global__ __launch_bounds__(256) void vsa_pool_kernel(const uint16_t* q, const uint16_t* k, int heads, int s_q,
+                                                       int s_kv, int nb_max, float* pooled_q, float* pooled_k) {
+  __shared__ float2 part[3][64];
   const int which = blockIdx.x & 1;
   const int rest = blockIdx.x >> 1;
   const int bh = rest / nb_max, blk = rest - bh * nb_max;
   const int s = which == 0 ? s_q : s_kv;
   const int nb = (s + kBlock - 1) / kBlock;
-  if (blk >= nb) return;
+  if (blk >= nb) return;   // uniform over the workgroup
   const uint16_t* x = which == 0 ? q : k;
   float* out = which == 0 ? pooled_q : pooled_k;
   const int b = bh / heads, h = bh - b * heads;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int t0 = blk * kBlock, t1 = min(t0 + kBlock, s);
-  const int64_t stride = (int64_t)heads * kHeadDim;
+  const int64_t stride = (int64_t)heads * (kHeadDim / 2);   // 32-bit words between tokens
   const unsigned* src = reinterpret_cast<const unsigned*>(x + ((int64_t)b * s * heads + h) * kHeadDim) + lane;
-  float a0 = 0.0f, a1 = 0.0f;
-  for (int t = t0; t < t1; ++t) {
-    const unsigned v = src[(int64_t)t * (stride / 2)];
-    a0 += __builtin_bit_cast(float, v << 16);
-    a1 += __builtin_bit_cast(float, v & 0xffff0000u);
+  unsigned v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + 16 * wv + i;
+    v[i] = t < t1 ? src[(int64_t)t * stride] : 0u;
   }
-  const float n = (float)(t1 - t0);
-  float* dst = out + ((int64_t)bh * nb + blk) * kHeadDim + 2 * lane;
-  dst[0] = __fdiv_rn(a0, n);
-  dst[1] = __fdiv_rn(a1, n);
+  float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    a0 += __builtin_bit_cast(float, v[i] << 16);
+    a1 += __builtin_bit_cast(float, v[i] & 0xffff0000u);
+  }
+  if (wv > 0) part[wv - 1][lane] = make_float2(a0, a1);
+  __syncthreads();
+  if (wv == 0) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w) {
+      a0 += part[w][lane].x;
+      a1 += part[w][lane].y;
+    }
+    const float n = (float)(t1 - t0);
+    float* dst = out + ((int64_t)bh * nb + blk) * kHeadDim + 2 * lane;
+    *reinterpret_cast<float2*>(dst) = make_float2(__fdiv_rn(a0, n), __fdiv_rn(a1, n));
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
-// Coarse stage 2: scores and top-keep selection of one query block (256 threads).  The score of
-// key block j is summed by 8 lanes, 16 consecutive channels each (in channel order), then across
-// the 8 lanes by a butterfly.  Scores and indices live in dynamic LDS, n_pow2 of each.
+// Coarse stage 2: scores and the top-keep selection of kSelQB consecutive query blocks of one
+// (batch, head) per workgroup (4 waves), so that each block mean of K is read once per kSelQB query
+// blocks.
+//  * Scores: 8 lanes per key block, 16 consecutive channels each (products summed in channel
+//    order), then a 3-level butterfly over the 8 lanes; score[i][j] = sum / sqrt(128), in LDS.
+//  * Selection of query block i (one wave): an order-preserving 32-bit key of each score (larger
+//    score, larger key; -0 taken as +0), a radix select over 4 digits of 8 bits from the top finds
+//    the keep-th largest key T and how many of the keys equal to T are taken; then one sweep in
+//    index order takes every key above T and the first of those equal to T -- ties to the lower
+//    index -- and writes their indices, ascending, by ballot prefix counts.
 constexpr int kSelThreads = 256;
-constexpr int kMaxKeyBlocks = 8192;
+constexpr int kSelQB = 8;
+constexpr int kMaxKeyBlocks = 4096;   // keys of kSelQB query blocks in LDS: 128 KB
 
-__device__ __forceinline__ bool ranks_before(float sa, int ia, float sb, int ib) {
-  return sa > sb || (sa == sb && ia < ib);
+__device__ __forceinline__ unsigned order_key(float f) {
+  if (f == 0.0f) f = 0.0f;   // -0 and +0 compare equal
+  const unsigned u = __builtin_bit_cast(unsigned, f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(const float* pooled_q, const float* pooled_k, int n_qb,
-                                                                 int n_kb, int n_pow2, int keep, int keep_pow2,
-                                                                 int* block_idx) {
-  extern __shared__ float sel_lds[];
-  float* score = sel_lds;
-  int* index = reinterpret_cast<int*>(sel_lds + n_pow2);
-  const int bh = blockIdx.x / n_qb, qb = blockIdx.x - bh * n_qb;
-  const int tid = threadIdx.x;
-  const int part = tid & 7;          // channels 16 part .. 16 part + 15
-  const int sub = tid >> 3;          // key block within a group of 32
-  float qm[16];
-  {
+                                                                 int n_kb, int groups_per_bh, int keep, int* block_idx) {
+  extern __shared__ unsigned sel_lds[];   // [kSelQB][n_kb] keys, then [4 waves][256] histograms
+  unsigned* keys = sel_lds;
+  unsigned* hist_all = sel_lds + kSelQB * n_kb;
+  const int bh = blockIdx.x / groups_per_bh;
+  const int qb0 = (blockIdx.x - bh * groups_per_bh) * kSelQB;
+  const int nq = min(kSelQB, n_qb - qb0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int part = tid & 7;   // channels 16 part .. 16 part + 15
+  const int sub = tid >> 3;   // key block within a pass of 32
+
+  // ---- scores
+  float qm[kSelQB][16];
+#pragma unroll
+  for (int i = 0; i < kSelQB; ++i) {
+    const int qb = qb0 + (i < nq ? i : 0);
     const float4* src = reinterpret_cast<const float4*>(pooled_q + ((int64_t)bh * n_qb + qb) * kHeadDim + 16 * part);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float4 x = src[i];
-      qm[4 * i] = x.x;
-      qm[4 * i + 1] = x.y;
-      qm[4 * i + 2] = x.z;
-      qm[4 * i + 3] = x.w;
+    for (int c = 0; c < 4; ++c) {
+      const float4 x = src[c];
+      qm[i][4 * c] = x.x;
+      qm[i][4 * c + 1] = x.y;
+      qm[i][4 * c + 2] = x.z;
+      qm[i][4 * c + 3] = x.w;
     }
   }
   const float* kmb = pooled_k + (int64_t)bh * n_kb * kHeadDim;
-  for (int j0 = 0; j0 < n_pow2; j0 += kSelThreads / 8) {
+  for (int j0 = 0; j0 < n_kb; j0 += kSelThreads / 8) {
     const int j = j0 + sub;
-    float acc = 0.0f;
-    if (j < n_kb) {
-      const float4* kr = reinterpret_cast<const float4*>(kmb + (int64_t)j * kHeadDim + 16 * part);
+    float km[16];
+    const float4* kr = reinterpret_cast<const float4*>(kmb + (int64_t)(j < n_kb ? j : 0) * kHeadDim + 16 * part);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 x = kr[i];
-        acc = __builtin_fmaf(qm[4 * i], x.x, acc);
-        acc = __builtin_fmaf(qm[4 * i + 1], x.y, acc);
-        acc = __builtin_fmaf(qm[4 * i + 2], x.z, acc);
-        acc = __builtin_fmaf(qm[4 * i + 3], x.w, acc);
-      }
+    for (int c = 0; c < 4; ++c) {
+      const float4 x = kr[c];
+      km[4 * c] = x.x;
+      km[4 * c + 1] = x.y;
+      km[4 * c + 2] = x.z;
+      km[4 * c + 3] = x.w;
     }
-    acc += __shfl_xor(acc, 1);
-    acc += __shfl_xor(acc, 2);
-    acc += __shfl_xor(acc, 4);
-    if (part == 0 && j < n_pow2) {
-      score[j] = j < n_kb ? acc * kInvSqrtD : -__builtin_inff();   // padding sorts last
-      index[j] = j < n_kb ? j : 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < kSelQB; ++i) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) acc = __builtin_fmaf(qm[i][c], km[c], acc);
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      acc += __shfl_xor(acc, 4);
+      if (part == 0 && j < n_kb) keys[i * n_kb + j] = order_key(acc * kInvSqrtD);
     }
   }
   __syncthreads();
-  // bitonic sort, order: ranks_before (larger score first, then lower index)
-  for (int size = 2; size <= n_pow2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < n_pow2; i += kSelThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;   // this half sorts in ranks_before order
-          const float si = score[i], sj = score[j];
-          const int ii = index[i], ij = index[j];
-          if (ranks_before(sj, ij, si, ii) == up) {
-            score[i] = sj;
-            score[j] = si;
-            index[i] = ij;
-            index[j] = ii;
-          }
-        }
+
+  // ---- selection, one query block per wave at a time
+  unsigned* hist = hist_all + 256 * wv;
+  const uint64_t lt_mask = (1ull << lane) - 1;
+  for (int i = wv; i < nq; i += 4) {
+    const unsigned* kk = keys + i * n_kb;
+    unsigned prefix = 0, mask = 0;
+    int need = keep;   // how many of the keys matching prefix/mask are still to be taken
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) hist[4 * lane + c] = 0;
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+      for (int j = lane; j < n_kb; j += 64) {
+        const unsigned key = kk[j];
+        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1u);
       }
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      // lane l owns digits 4l .. 4l+3; counts of larger digits: lanes above, then higher bins
+      unsigned h4[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) h4[c] = hist[4 * lane + c];
+      const unsigned mine = h4[0] + h4[1] + h4[2] + h4[3];
+      unsigned inc = mine;   // inclusive suffix sum over lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const unsigned y = __shfl_down(inc, d);
+        if (lane + d < 64) inc += y;
+      }
+      const unsigned above = inc - mine;   // keys whose digit belongs to a higher lane
+      int digit = -1, new_need = 0;
+      unsigned acc = above;
+#pragma unroll
+      for (int c = 3; c >= 0; --c) {
+        if (digit < 0 && acc < (unsigned)need && acc + h4[c] >= (unsigned)need) {
+          digit = 4 * lane + c;
+          new_need = need - (int)acc;
+        }
+        acc += h4[c];
+      }
+      const uint64_t found = __ballot(digit >= 0);
+      const int src_lane = __builtin_ctzll(found);
+      digit = __shfl(digit, src_lane);
+      need = __shfl(new_need, src_lane);
+      prefix |= (unsigned)digit << shift;
+      mask |= 255u << shift;
+    }
+    // prefix is now the keep-th largest key T; take all keys > T and the first `need` equal to it
+    int* dst = block_idx + ((int64_t)bh * n_qb + qb0 + i) * keep;
+    int taken = 0, eq_seen = 0;
+    for (int j0 = 0; j0 < n_kb; j0 += 64) {
+      const int j = j0 + lane;
+      const unsigned key = j < n_kb ? kk[j] : 0u;
+      const bool eq = j < n_kb && key == prefix;
+      const uint64_t eqm = __ballot(eq);
+      const int eq_rank = eq_seen + __popcll(eqm & lt_mask);
+      const bool take = j < n_kb && (key > prefix || (eq && eq_rank < need));
+      const uint64_t tm = __ballot(take);
+      const int pos = taken + __popcll(tm & lt_mask);
+      if (take && pos < keep) dst[pos] = j;   // exactly keep are taken; the bound only guards the list
+      taken += __popcll(tm);
+      eq_seen += __popcll(eqm);
     }
   }
-  // the first `keep` entries, sorted ascending by index (the rest of the keep_pow2 window padded)
-  for (int i = tid; i < keep_pow2; i += kSelThreads) index[i] = i < keep ? index[i] : 0x7fffffff;
-  __syncthreads();
-  for (int size = 2; size <= keep_pow2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = tid; i < keep_pow2; i += kSelThreads) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const bool up = (i & size) == 0;
-          const int a = index[i], c = index[j];
-          if ((c < a) == up) {
-            index[i] = c;
-            index[j] = a;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-  int* dst = block_idx + ((int64_t)bh * n_qb + qb) * keep;
-  for (int i = tid; i < keep; i += kSelThreads) dst[i] = index[i];
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -398,12 +453,6 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
   }
 }
 
-int pow2_at_least(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
-
 }  // namespace
 
 size_t vsa_select_scratch_bytes(const AttnShape& sh) {
@@ -420,21 +469,21 @@ hipError_t launch_vsa_select(const void* q, const void* k, const AttnShape& sh, 
   float* pooled_q = static_cast<float*>(scratch);
   float* pooled_k = pooled_q + bh * n_qb * kHeadDim;
   const int nb_max = n_qb > n_kb ? n_qb : n_kb;
-  hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)(2 * bh * nb_max)), dim3(64), 0, stream,
+  hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)(2 * bh * nb_max)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), (int)sh.heads, (int)sh.s_q,
                      (int)sh.s_kv, nb_max, pooled_q, pooled_k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int n_pow2 = pow2_at_least(n_kb > 32 ? n_kb : 32);
-  const unsigned lds = (unsigned)n_pow2 * 8;
-  if (lds > 65536) return hipErrorInvalidValue;
+  if (n_kb > kMaxKeyBlocks) return hipErrorInvalidValue;
+  const unsigned lds = (unsigned)(kSelQB * n_kb + 4 * 256) * 4;   // at most 132 KB
   if (lds > 32768) {   // above the default dynamic LDS limit of some runtimes: raise it explicitly
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(vsa_select_kernel),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)(n_qb * bh)), dim3(kSelThreads), lds, stream, pooled_q,
-                     pooled_k, n_qb, n_kb, n_pow2, keep, pow2_at_least(keep), block_idx);
+  const int groups = (n_qb + kSelQB - 1) / kSelQB;
+  hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)(groups * bh)), dim3(kSelThreads), lds, stream, pooled_q,
+                     pooled_k, n_qb, n_kb, groups, keep, block_idx);
   return hipGetLastError();
 }
 
