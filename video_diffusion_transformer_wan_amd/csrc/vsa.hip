@@ -260,9 +260,13 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(const float* po
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fine stage.
-constexpr int kAttnWaves = 4;
-constexpr int kKBytes = kBlock * kHeadDim * 2;   // K tile, 16 KB
+// Fine stage.  A workgroup of 8 waves serves 4 query blocks, one wave pair each (32 query rows per
+// wave); each pair streams the 32-key halves of its selected key blocks through its own 2-stage LDS
+// ring, so every SIMD holds two waves of different pairs.
+constexpr int kAttnWaves = 8;
+constexpr int kPairs = kAttnWaves / 2;
+constexpr int kHalf = 32;                        // keys per step
+constexpr int kKBytes = kHalf * kHeadDim * 2;    // K of one step, 8 KB
 constexpr int kStageBytes = 2 * kKBytes;         // [K | V]
 constexpr int kPairLds = 2 * kStageBytes;        // 2 stages per wave pair
 
@@ -272,35 +276,36 @@ struct VsaParams {
   const uint16_t* v;
   const int* block_idx;   // [bh][n_qb][keep]
   uint16_t* o;
-  int heads, s_q, s_kv, n_qb, n_kb, keep, pairs_per_bh;
+  int heads, s_q, s_kv, n_qb, n_kb, keep, groups_per_bh;
 };
 
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kPairLds];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kPairs * kPairLds];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wv >> 1, w2 = wv & 1;
   const int l32 = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.x / p.pairs_per_bh;
-  const int qb = 2 * (blockIdx.x - bh * p.pairs_per_bh) + pair;
+  const int bh = blockIdx.x / p.groups_per_bh;
+  const int qb = kPairs * (blockIdx.x - bh * p.groups_per_bh) + pair;
   const bool active = qb < p.n_qb;                  // wave-uniform
   const int bb = bh / p.heads, hh = bh - bb * p.heads;
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
   unsigned char* ring = smem + pair * kPairLds;
   const unsigned lds_ring = (unsigned)(uintptr_t)(lds_void_t*)ring;
 
-  // loads: wave w2 of the pair writes 1 KB blocks 8 w2 .. 8 w2 + 7 of the K tile and of the V tile
-  unsigned k_src[8], v_src[8];
+  // loads: wave w2 of the pair writes 1 KB blocks 4 w2 .. 4 w2 + 3 (4 key rows each) of the K and
+  // of the V part of a stage; K rows permuted by swap23 and chunks XOR-swizzled by row % 16, V rows
+  // in key order with chunks XOR-swizzled by 4 (row % 4) -- the bf16 forward's layouts
+  unsigned k_src[4], v_src[4];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int m = 8 * w2 + it;
+  for (int it = 0; it < 4; ++it) {
+    const int m = 4 * w2 + it;
     const int row = 4 * m + (lane >> 4);
     const int pch = lane & 15;
     k_src[it] = (unsigned)(swap23(row) * stride + 16 * (pch ^ (row & 15)));
     v_src[it] = (unsigned)(row * stride + 16 * (pch ^ ((row & 3) << 2)));
   }
-  // operand read offsets (the bf16 forward's): K rows l32 (+32), V by transposing reads
   const int k_rd0 = l32 * 256 + 16 * ((h ^ l32) & 1) + 32 * ((l32 >> 1) & 7);
   int v_rd0;
   {
@@ -313,6 +318,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kv_head;
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kv_head;
   const int* list = p.block_idx + ((int64_t)bh * p.n_qb + (active ? qb : 0)) * p.keep;
+  const int n_steps = 2 * p.keep;
 
   // Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7 (rows past s_q read zeros)
   const int q0 = qb * kBlock + 32 * w2;
@@ -328,16 +334,22 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
           bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(qr, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
   }
 
-  auto issue = [&](int j) __attribute__((always_inline)) {
-    const int blk = list[j];
-    const bool ok = active && blk >= 0 && blk < p.n_kb;   // anything else reads as zeros
-    const int64_t off = (int64_t)(ok ? blk : 0) * kBlock * stride;
-    const int64_t bytes = ok ? (int64_t)(p.s_kv - 1 - blk * kBlock) * stride + kHeadDim * 2 : 0;
+  // first key of step t (-1: nothing to attend: an index outside [0, n_kb), a half past s_kv, or
+  // an idle pair)
+  auto step_key0 = [&](int t) __attribute__((always_inline)) {
+    const int blk = list[t >> 1];
+    const int kv0 = blk * kBlock + kHalf * (t & 1);
+    return (active && blk >= 0 && blk < p.n_kb && kv0 < p.s_kv) ? kv0 : -1;
+  };
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int kv0 = step_key0(t);
+    const int64_t off = (int64_t)(kv0 >= 0 ? kv0 : 0) * stride;
+    const int64_t bytes = kv0 >= 0 ? (int64_t)(p.s_kv - 1 - kv0) * stride + kHeadDim * 2 : 0;
     const u32x4_t kr = rsrc_words(kbase + off, bytes);
     const u32x4_t vr = rsrc_words(vbase + off, bytes);
-    const unsigned st = lds_ring + (unsigned)((j & 1) * kStageBytes + 8192 * w2);
+    const unsigned st = lds_ring + (unsigned)((t & 1) * kStageBytes + 4096 * w2);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
+    for (int it = 0; it < 4; ++it) {
       dma_b128(kr, st + 1024 * it, k_src[it]);
       dma_b128(vr, st + kKBytes + 1024 * it, v_src[it]);
     }
@@ -353,44 +365,30 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
   issue(0);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   barrier();
-  for (int j = 0; j < p.keep; ++j) {
-    if (j + 1 < p.keep) issue(j + 1);
-    const int blk = list[j];
-    if (active && blk >= 0 && blk < p.n_kb) {   // an index outside [0, n_kb) is skipped
-      const unsigned char* ks = ring + (j & 1) * kStageBytes;
-      // S^T of the block: s[kb] holds keys 32 kb + swap23(8 (r / 4) + 4 h + r % 4) of the lane's row
-      f32x16_t s[2];
+  for (int t = 0; t < n_steps; ++t) {
+    if (t + 1 < n_steps) issue(t + 1);
+    const int kv0 = step_key0(t);
+    if (kv0 >= 0) {
+      const unsigned char* ks = ring + (t & 1) * kStageBytes;
+      // S^T of the 32 keys: s holds key kv0 + swap23(8 (r / 4) + 4 h + r % 4) of the lane's row
+      f32x16_t s;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) s[r] = 0.0f;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        const int o0 = k_rd0 ^ (64 * st), o1 = k_rd0 ^ (64 * st + 32);
-        const bf16x8_t f0 = *reinterpret_cast<const bf16x8_t*>(ks + o0);
-        const bf16x8_t f1 = *reinterpret_cast<const bf16x8_t*>(ks + o0 + 8192);
-        const bf16x8_t f2 = *reinterpret_cast<const bf16x8_t*>(ks + o1);
-        const bf16x8_t f3 = *reinterpret_cast<const bf16x8_t*>(ks + o1 + 8192);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[2 * st], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[2 * st], s[1], 0, 0, 0);
-        s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f2, qf[2 * st + 1], s[0], 0, 0, 0);
-        s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f3, qf[2 * st + 1], s[1], 0, 0, 0);
+        const bf16x8_t f0 = *reinterpret_cast<const bf16x8_t*>(ks + (k_rd0 ^ (64 * st)));
+        const bf16x8_t f1 = *reinterpret_cast<const bf16x8_t*>(ks + (k_rd0 ^ (64 * st + 32)));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, qf[2 * st], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1, qf[2 * st + 1], s, 0, 0, 0);
       }
-      // keys past s_kv (the last block only) get a score that exp2 turns into 0
-      const int kv0 = blk * kBlock;
-      if (kv0 + kBlock > p.s_kv) {
+      if (kv0 + kHalf > p.s_kv) {   // keys past s_kv get a score that exp2 turns into 0
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kv0 + swap23(32 * kb + 8 * (r >> 2) + 4 * h + (r & 3)) >= p.s_kv) s[kb][r] = kNeg;
+        for (int r = 0; r < 16; ++r)
+          if (kv0 + swap23(8 * (r >> 2) + 4 * h + (r & 3)) >= p.s_kv) s[r] = kNeg;
       }
-      // online softmax: the row max over both halves of the row, rescale when it grows
       float mx = kNeg;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[kb][r]);
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[r]);
       float ma, mb;
       pair_values(mx, ma, mb);
       const float m_new = __builtin_fmaxf(m, __builtin_fmaxf(ma, mb));
@@ -404,25 +402,22 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
       }
       m = m_new;
       const float mc = m * kScaleLog2;
-      unsigned pk[2][8];
+      unsigned pk[8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], kScaleLog2, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], kScaleLog2, -mc));
+        pk[r >> 1] = cvt_pk_bf16(p0, p1);
+        l += p0 + p1;
+      }
+      // O^T += V^T P^T over the step's 2 groups of 16 keys
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], kScaleLog2, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], kScaleLog2, -mc));
-          pk[kb][r >> 1] = cvt_pk_bf16(p0, p1);
-          l += p0 + p1;
-        }
-      // O^T += V^T P^T over the block's 4 steps of 16 keys
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = t >> 1, u = t & 1;
-        const u32x4_t x = {pk[kb][4 * u], pk[kb][4 * u + 1], pk[kb][4 * u + 2], pk[kb][4 * u + 3]};
+      for (int u = 0; u < 2; ++u) {
+        const u32x4_t x = {pk[4 * u], pk[4 * u + 1], pk[4 * u + 2], pk[4 * u + 3]};
         const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const unsigned char* vp = ks + (v_rd0 ^ (64 * db)) + 4096 * t;
+          const unsigned char* vp = ks + (v_rd0 ^ (64 * db)) + 4096 * u;
           const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp));
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vp + 1024));
           const i16x4_t cat[2] = {lo, hi};
@@ -430,8 +425,8 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
         }
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of block j+1
-    barrier();                              // block j+1 has landed; everyone is done with block j
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);   // this wave's loads of step t+1
+    barrier();                              // step t+1 has landed; everyone is done with step t
   }
 
   if (active) {
@@ -501,8 +496,8 @@ hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, const in
   p.n_qb = (int)ceil_div(sh.s_q, kBlock);
   p.n_kb = (int)ceil_div(sh.s_kv, kBlock);
   p.keep = keep;
-  p.pairs_per_bh = (p.n_qb + 1) / 2;
-  const int64_t grid = sh.batch * sh.heads * p.pairs_per_bh;
+  p.groups_per_bh = (p.n_qb + kPairs - 1) / kPairs;
+  const int64_t grid = sh.batch * sh.heads * p.groups_per_bh;
   hipLaunchKernelGGL(vsa_attn_kernel, dim3((unsigned)grid), dim3(64 * kAttnWaves), 0, stream, p);
   return hipGetLastError();
 }
