@@ -230,13 +230,14 @@ def run_vsa(name, steps, warmup):
     keys = torch.clamp(s - 64 * idx.long(), max=64).sum(dim=-1)                  # [b, H, n_qb]
     rows = torch.clamp(s - 64 * torch.arange(n_qb, device="cuda"), max=64)      # [n_qb]
     flops = float(4 * d * (keys * rows).sum().item())
+    gathered = float(keys.sum().item()) * 2 * d * 2    # K and V rows of the attended keys, per query block
     tf = flops / (ms * 1e-3) / 1e12
     ftf = flops / (fine_ms * 1e-3) / 1e12
     return {"workload": name, "path": "vsa block-sparse bf16", "batch": b, "heads": H, "s": s, "keep": w.keep,
             "sparsity": 1.0 - w.keep / -(-s // 64), "ms": ms, "tflops": tf, "fine_ms": fine_ms,
             "fine_tflops": ftf, "fine_frac_of_peak": ftf / PEAK_TFLOPS["bf16"], "coarse_ms": coarse_ms,
             "dense_ms": dense_ms, "speedup_vs_dense": dense_ms / ms, "fine_speedup_vs_dense": dense_ms / fine_ms,
-            "flops": flops}
+            "flops": flops, "gathered_bytes": gathered, "gather_tbps": gathered / (fine_ms * 1e-3) / 1e12}
 
 
 def main():
