@@ -11,11 +11,11 @@
 //  * vsa_select_kernel -- one workgroup per 8 query blocks of one batch*head: their block scores
 //    against all key blocks in fp32, and per query block a radix select of the top `keep` (larger
 //    score first, then lower index), written in ascending index order.
-//  * vsa_attn_kernel -- one workgroup = 4 waves = 2 query blocks (a wave pair each, 32 query rows
-//    per wave); each pair streams the K and V tiles of its selected key blocks through its own
-//    2-stage LDS ring (direct-to-LDS loads), with the bf16 forward's transposed products, LDS
-//    layouts and swizzles (S^T = K Q^T; O^T += V^T P^T by transposing V reads) and an online
-//    softmax with a running row max (the O accumulators rescaled only when some row's max grows).
+//  * vsa_attn_kernel -- one workgroup = one wave pair = one query block (32 query rows per wave);
+//    the pair streams the 32-key halves of its selected key blocks through a 2-stage LDS ring
+//    (direct-to-LDS loads), with the bf16 forward's transposed products, LDS layouts and swizzles
+//    (S^T = K Q^T; O^T += V^T P^T by transposing V reads) and an online softmax with a running row
+//    max (the O accumulators rescaled only when some row's max grows).
 
 #include "wan_attn_internal.h"
 
@@ -260,10 +260,10 @@ __global__ __launch_bounds__(kSelThreads) void vsa_select_kernel(const float* po
 }
 
 // ---------------------------------------------------------------------------------------------
-// Fine stage.  A workgroup of 8 waves serves 4 query blocks, one wave pair each (32 query rows per
-// wave); each pair streams the 32-key halves of its selected key blocks through its own 2-stage LDS
-// ring, so every SIMD holds two waves of different pairs.
-constexpr int kAttnWaves = 8;
+// Fine stage.  A workgroup is one wave pair serving one query block (32 query rows per wave), with
+// its own 2-stage LDS ring of 32-key steps (32 KB): up to 5 workgroups per CU, each synchronising
+// only its own two waves, so query blocks whose lists differ do not wait for each other.
+constexpr int kAttnWaves = 2;
 constexpr int kPairs = kAttnWaves / 2;
 constexpr int kHalf = 32;                        // keys per step
 constexpr int kKBytes = kHalf * kHeadDim * 2;    // K of one step, 8 KB
