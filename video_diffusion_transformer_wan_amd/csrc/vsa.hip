@@ -277,7 +277,14 @@ struct VsaParams {
   const int* block_idx;   // [bh][n_qb][keep]
   uint16_t* o;
   int heads, s_q, s_kv, n_qb, n_kb, keep, groups_per_bh;
+  int total;   // workgroups with work: batch*heads*groups_per_bh
 };
+
+// Workgroup numbering: workgroup w runs on XCD w % 8, and each run of 8 * kXcdChunk consecutive query
+// blocks gives every XCD kXcdChunk consecutive ones.  All XCDs stay on about the same head (its K and
+// V stay in the shared last-level cache), while each XCD's L2 serves neighbouring query blocks,
+// whose selections overlap when the scores have locality.
+constexpr int kXcdChunk = 64;
 
 __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kPairs * kPairLds];
@@ -286,8 +293,12 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wv >> 1, w2 = wv & 1;
   const int l32 = lane & 31, h = lane >> 5;
-  const int bh = blockIdx.x / p.groups_per_bh;
-  const int qb = kPairs * (blockIdx.x - bh * p.groups_per_bh) + pair;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int round8 = slot / kXcdChunk;
+  const int item = (8 * round8 + xcd) * kXcdChunk + (slot - round8 * kXcdChunk);
+  if (item >= p.total) return;
+  const int bh = item / p.groups_per_bh;
+  const int qb = kPairs * (item - bh * p.groups_per_bh) + pair;
   const bool active = qb < p.n_qb;                  // wave-uniform
   const int bb = bh / p.heads, hh = bh - bb * p.heads;
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;   // bytes between tokens
@@ -497,7 +508,9 @@ hipError_t launch_vsa_attn(const void* q, const void* k, const void* v, const in
   p.n_kb = (int)ceil_div(sh.s_kv, kBlock);
   p.keep = keep;
   p.groups_per_bh = (p.n_qb + kPairs - 1) / kPairs;
-  const int64_t grid = sh.batch * sh.heads * p.groups_per_bh;
+  p.total = (int)(sh.batch * sh.heads * p.groups_per_bh);
+  const int64_t chunk8 = 8LL * kXcdChunk;
+  const int64_t grid = (p.total + chunk8 - 1) / chunk8 * chunk8;
   hipLaunchKernelGGL(vsa_attn_kernel, dim3((unsigned)grid), dim3(64 * kAttnWaves), 0, stream, p);
   return hipGetLastError();
 }
