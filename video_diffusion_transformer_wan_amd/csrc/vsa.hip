@@ -30,6 +30,10 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
+// Read-only data that every lane of a wave reads at the same index (the block lists), through the
+// constant address space: the compiler loads it with scalar loads, whose completion counter is not
+// the one the direct-to-LDS loads use, so reading an entry never waits for the K/V loads in flight.
+typedef __attribute__((address_space(4))) const int const_int_t;
 
 constexpr int kBlock = 64;
 constexpr float kNeg = -1.0e30f;
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
   const int64_t kv_head = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kv_head;
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kv_head;
-  const int* list = p.block_idx + ((int64_t)bh * p.n_qb + (active ? qb : 0)) * p.keep;
+  const const_int_t* list = (const const_int_t*)(p.block_idx + ((int64_t)bh * p.n_qb + (active ? qb : 0)) * p.keep);
   const int n_steps = 2 * p.keep;
 
   // Q^T operand: lane holds query row q0 + l32, channels 16c + 8h .. +7 (rows past s_q read zeros)
@@ -352,8 +356,7 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
     const int kv0 = blk * kBlock + kHalf * (t & 1);
     return (active && blk >= 0 && blk < p.n_kb && kv0 < p.s_kv) ? kv0 : -1;
   };
-  auto issue = [&](int t) __attribute__((always_inline)) {
-    const int kv0 = step_key0(t);
+  auto issue = [&](int t, int kv0) __attribute__((always_inline)) {
     const int64_t off = (int64_t)(kv0 >= 0 ? kv0 : 0) * stride;
     const int64_t bytes = kv0 >= 0 ? (int64_t)(p.s_kv - 1 - kv0) * stride + kHeadDim * 2 : 0;
     const u32x4_t kr = rsrc_words(kbase + off, bytes);
@@ -373,12 +376,16 @@ __global__ __launch_bounds__(64 * kAttnWaves, 1) void vsa_attn_kernel(const VsaP
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float m = kNeg, l = 0.0f;
 
-  issue(0);
+  int kv_next = step_key0(0);
+  issue(0, kv_next);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   barrier();
   for (int t = 0; t < n_steps; ++t) {
-    if (t + 1 < n_steps) issue(t + 1);
-    const int kv0 = step_key0(t);
+    const int kv0 = kv_next;   // first key of this step, read when its loads were issued
+    if (t + 1 < n_steps) {
+      kv_next = step_key0(t + 1);
+      issue(t + 1, kv_next);
+    }
     if (kv0 >= 0) {
       const unsigned char* ks = ring + (t & 1) * kStageBytes;
       // S^T of the 32 keys: s holds key kv0 + swap23(8 (r / 4) + 4 h + r % 4) of the lane's row
