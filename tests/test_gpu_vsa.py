@@ -204,3 +204,20 @@ def test_wan_workload_sampled(name):
     ref = bs.sparse_attention_rows(qn, kn, vn, sel_np, rows)
     got = to_np(o.index_select(2, hsel))[rows[:, 0], rows[:, 2], rows[:, 1]]
     _check_output(got, ref)
+
+
+def test_largest_key_block_count():
+    # 4,096 key blocks (262,144 keys), the selection's largest: the scores of its 8 query blocks fill
+    # 128 KB of LDS (the launch raises the dynamic LDS limit)
+    b, H, s_q, s_kv, keep = 1, 1, 100, 4096 * 64, 512
+    print(f"vsa b={b} H={H} s_q={s_q} s_kv={s_kv} keep={keep}", flush=True)
+    q, k, v = wan_inputs.random_qkv(b, H, s_q, s_kv, 41003 + keep, device="cuda")
+    sel = wan.vsa_select(q, k, keep)
+    o = wan.vsa_attention(q, k, v, sel)
+    torch.cuda.synchronize()
+    # float64 copies made by torch (exact for bf16; numpy's own cast of large torch-backed arrays is slow)
+    qn, kn, vn = (t.double().cpu().numpy() for t in (q, k, v))
+    sel_np = sel.cpu().numpy().astype(np.int64)
+    _check_selection(sel_np, qn, kn, keep)
+    rows = _all_rows(b, H, s_q)[::7]
+    _check_output(_gather(o, rows), bs.sparse_attention_rows(qn, kn, vn, sel_np, rows))
