@@ -51,6 +51,7 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, r);
 }
 
+// Values of lanes l and l^32 (the two halves of one query row's keys).
 __device__ __forceinline__ void pair_values(float x, float& a, float& b) {
   const unsigned u = __builtin_bit_cast(unsigned, x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
@@ -72,10 +73,14 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void* base, int64_t bytes) {
   return r;
 }
 
+// Direct global -> LDS load of 16 bytes per lane (lane i's bytes land at lds_addr + 16 i).  Inline asm,
+// so that the compiler does not make LDS reads of the other ring stage wait for it; the kernel waits
+// for these loads itself (s_waitcnt vmcnt) before the barrier after which its waves read them.
 __device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
 }
 
+// Workgroup barrier without __syncthreads()'s release fence (which would wait for the loads in flight).
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------------
