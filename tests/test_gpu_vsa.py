@@ -221,3 +221,19 @@ def test_largest_key_block_count():
     _check_selection(sel_np, qn, kn, keep)
     rows = _all_rows(b, H, s_q)[::7]
     _check_output(_gather(o, rows), bs.sparse_attention_rows(qn, kn, vn, sel_np, rows))
+
+
+def test_many_query_blocks_every_row():
+    # 8 heads x 65 query blocks = 520 workgroups: more than one round of the XCD numbering (8 x 64), with
+    # rounds that straddle heads; every output row is checked
+    b, H, s_q, s_kv, keep = 1, 8, 4160, 640, 2
+    print(f"vsa b={b} H={H} s_q={s_q} s_kv={s_kv} keep={keep}", flush=True)
+    q, k, v = wan_inputs.random_qkv(b, H, s_q, s_kv, 41004, device="cuda")
+    sel = wan.vsa_select(q, k, keep)
+    o = wan.vsa_attention(q, k, v, sel)
+    torch.cuda.synchronize()
+    qn, kn, vn = (t.double().cpu().numpy() for t in (q, k, v))
+    sel_np = sel.cpu().numpy().astype(np.int64)
+    _check_selection(sel_np, qn, kn, keep)
+    rows = _all_rows(b, H, s_q)
+    _check_output(_gather(o, rows), bs.sparse_attention_rows(qn, kn, vn, sel_np, rows))
