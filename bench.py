@@ -75,7 +75,21 @@ def time_calls(fn, steps, warmup, stream):
 
 
 def cpu_baseline(w, q, k, v, budget_s=12.0):
-    """The oracle as it stands, on a bounded sample of seeded query rows of the workload."""
+    """The oracle as it stands, on a bounded sample of seeded query rows of the workload: with every BLAS
+    thread, then (a smaller sample) with one."""
+    res = _cpu_baseline_run(w, q, k, v, budget_s)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = _cpu_baseline_run(w, q, k, v, budget_s / 3)
+        res["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"],
+                                "seconds": one["seconds"]}
+    except Exception as e:  # report, do not hide the baseline
+        res["single_thread"] = {"error": str(e)}
+    return res
+
+
+def _cpu_baseline_run(w, q, k, v, budget_s):
     import numpy as np
     import oracle
     import wan_inputs
