@@ -1,6 +1,7 @@
 """Benchmark of the Wan DiT attention forward on one MI355X.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu]
+python bench.py --backward-only NAME | --linear-only NAME | --vsa-only NAME   (one path alone, for profiling)
 
 One step = one call of the C ABI's wan_attn_fwd on the workload's full shape, inputs already in
 HBM.  Prints ONE JSON line: the headline is the bf16 self-attention of the Wan-14B-shaped 720p,
