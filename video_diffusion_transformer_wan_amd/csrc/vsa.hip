@@ -483,22 +483,31 @@ int vsa_max_key_blocks() { return kMaxKeyBlocks; }
 hipError_t launch_vsa_select(const void* q, const void* k, const AttnShape& sh, int keep, int* block_idx,
                              void* scratch, hipStream_t stream) {
   const int n_qb = (int)ceil_div(sh.s_q, kBlock), n_kb = (int)ceil_div(sh.s_kv, kBlock);
+  if (n_kb > kMaxKeyBlocks) return hipErrorInvalidValue;
   const int64_t bh = sh.batch * sh.heads;
   float* pooled_q = static_cast<float*>(scratch);
   float* pooled_k = pooled_q + bh * n_qb * kHeadDim;
+  const unsigned lds = (unsigned)(kSelQB * n_kb + 4 * 256) * 4;   // at most 132 KB
+  hipError_t e;
+  if (lds > 32768) {   // above the default dynamic LDS limit of some runtimes: raised once per device
+    static bool raised[64] = {};
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!raised[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(vsa_select_kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kSelQB * kMaxKeyBlocks + 4 * 256) * 4);
+      if (e != hipSuccess) return e;
+      raised[dev] = true;
+    }
+  }
   const int nb_max = n_qb > n_kb ? n_qb : n_kb;
   hipLaunchKernelGGL(vsa_pool_kernel, dim3((unsigned)(2 * bh * nb_max)), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), (int)sh.heads, (int)sh.s_q,
                      (int)sh.s_kv, nb_max, pooled_q, pooled_k);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (n_kb > kMaxKeyBlocks) return hipErrorInvalidValue;
-  const unsigned lds = (unsigned)(kSelQB * n_kb + 4 * 256) * 4;   // at most 132 KB
-  if (lds > 32768) {   // above the default dynamic LDS limit of some runtimes: raise it explicitly
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(vsa_select_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   const int groups = (n_qb + kSelQB - 1) / kSelQB;
   hipLaunchKernelGGL(vsa_select_kernel, dim3((unsigned)(groups * bh)), dim3(kSelThreads), lds, stream, pooled_q,
                      pooled_k, n_qb, n_kb, groups, keep, block_idx);
