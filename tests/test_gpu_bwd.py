@@ -114,3 +114,37 @@ def test_backward_wan_sized():
     rel = float((sum_dv - sum_do).norm() / sum_do.norm())
     print(f"  sum dK / sum |dK| max {float((dk64.abs() / scale).max()):.2e}, sum dV vs sum dO rel {rel:.2e}")
     assert rel < 1e-2
+
+
+def test_backward_wan14b_720p_bench_inputs():
+    # the backward the bench times: Wan-14B-shaped 720p, 81 frames, b=2, with the bench's own inputs
+    # (make_qkv of the workload, dO from a generator seeded with the workload seed + 11)
+    w = wan_inputs.WORKLOADS["wan14b_720p81f_self"]
+    b, H, s = w.batch, w.heads, w.s_q
+    print(f"backward b={b} H={H} s={s}", flush=True)
+    q, k, v = wan_inputs.make_qkv(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
+    d_o = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o, lse = wan.attention_with_lse(q, k, v)
+    dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
+    torch.cuda.synchronize()
+    # sampled dQ rows on 4 heads of both batch entries (the first and last rows among them), against
+    # the oracle on host copies of those heads only
+    heads = [0, 13, 27, H - 1]
+    rng = np.random.default_rng(w.seed + 12)
+    rows = np.stack([rng.integers(0, b, 32), rng.integers(0, len(heads), 32), rng.integers(0, s, 32)], 1)
+    rows[0] = [0, 0, 0]
+    rows[1] = [b - 1, len(heads) - 1, s - 1]
+    hsel = torch.tensor(heads, device="cuda")
+    sub = [t.index_select(2, hsel).double().cpu().numpy() for t in (q, k, v, d_o)]
+    ref = oracle.dq_rows(*sub, rows)
+    got = dq.index_select(2, hsel).double().cpu().numpy()[rows[:, 0], rows[:, 2], rows[:, 1]]
+    _check_grad("dq rows", got, ref)
+    # identities over the whole tensors: sum over keys of dK is zero; sum over keys of dV is the sum
+    # over queries of dO (per batch entry, head and channel)
+    dk_sum = dk.double().sum(dim=1)
+    dk_scale = dk.double().abs().sum(dim=1)
+    ratio = float((dk_sum.abs() / dk_scale).max())
+    rel = float((dv.double().sum(dim=1) - d_o.double().sum(dim=1)).norm() / d_o.double().sum(dim=1).norm())
+    print(f"  sum dK / sum |dK| max {ratio:.2e}, sum dV vs sum dO rel {rel:.2e}", flush=True)
+    assert ratio < 2e-2 and rel < 1e-2
