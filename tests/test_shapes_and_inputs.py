@@ -83,3 +83,16 @@ def test_outliers_scale_the_chosen_columns():
     mask = torch.zeros(512, dtype=torch.bool)
     mask[cols] = True
     assert std[mask].min() > 4 and std[~mask].max() < 2
+
+
+def test_vsa_workloads_and_default_keep():
+    # the block-sparse workloads: the 16x28x52 token grid and the 720p 81-frame sequence, 87.5% of the
+    # 64-token key blocks dropped; the binding's default keep is the oracle's
+    import oracle.block_sparse as bs
+    import video_diffusion_transformer_wan_amd as wan
+    assert wan_inputs.VSA_WORKLOADS["wan1.3b_vsa_16x28x52"].s == 16 * 28 * 52
+    assert wan_inputs.VSA_WORKLOADS["wan14b_720p81f_vsa"].s == shapes.video_tokens(80, 720, 1280)
+    for w in wan_inputs.VSA_WORKLOADS.values():
+        assert w.keep == bs.default_keep(w.s)
+    for s in (1, 63, 64, 65, 512, 513, 4096, 23296, 32760, 75600, 262144):
+        assert wan.vsa_default_keep(s) == bs.default_keep(s), s
