@@ -24,7 +24,7 @@ the 8-bit GPU path, which is written separately):
 
 Quantisation decisions (steps 1-3) are taken in float32, as the GPU path takes them, so that the
 int8 and e4m3 codes can be compared bit for bit.  Steps 4-8 run in float64: this emulator is a
-diagnostic reference; the judged reference for the 8-bit path is still the exact attention.
+diagnostic reference; the 8-bit path's accuracy bounds are still taken against the exact attention.
 """
 
 import numpy as np

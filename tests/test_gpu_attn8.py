@@ -6,7 +6,7 @@
 * Stage 2 against the step-by-step 8-bit emulator of the oracle: they differ only in fp32
   summation order and the hardware exp2, so they must agree to rel-L2 <= 5e-3 (a diagnostic bound
   of this repository).
-* The judged bounds against the exact fp64 attention: rel-L2 <= 6e-2 and cosine >= 0.995.
+* The accuracy bounds against the exact fp64 attention: rel-L2 <= 6e-2 and cosine >= 0.995.
 """
 
 import numpy as np

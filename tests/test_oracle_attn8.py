@@ -6,7 +6,7 @@
 * Smoothing balances the per-channel maxima of Q' and K' and leaves QK^T unchanged (fp64 check).
 * Special cases that reduce to the exact attention: one key returns its V row; with exactly
   representable operands the only error left is the FP8 rounding of P, bounded by 2^-4 * max|V|.
-* The judged 8-bit bounds of the task (rel-L2 <= 6e-2, cosine >= 0.995 against exact attention) on
+* The 8-bit path's accuracy bounds (rel-L2 <= 6e-2, cosine >= 0.995 against exact attention) on
   a small seeded workload with 1% outlier channels at 8 sigma, and that the literal scheme without
   smoothing is worse there.
 """
@@ -125,7 +125,7 @@ def _outlier_case(seed, H=4, s=8192, d=128, n_rows=48):
     return q, k, v, rows
 
 
-def test_judged_bounds_with_outliers_and_literal_scheme_is_worse():
+def test_accuracy_bounds_with_outliers_and_literal_scheme_is_worse():
     q, k, v, rows = _outlier_case(9)
     ref = oracle.attention_rows(q, k, v, rows)
     rel_s, cos_s = _metrics(oracle.attn8_emulate(q, k, v, rows, smooth=True), ref)
