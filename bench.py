@@ -75,6 +75,23 @@ def time_calls(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps
 
 
+def step_stats(fn, steps, stream):
+    """Median and minimum of `steps` individually timed calls (HIP events on `stream`), in ms; run after
+    the timed region, which they do not change."""
+    import statistics
+    import torch
+    times = []
+    for _ in range(max(1, steps)):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return statistics.median(times), min(times)
+
+
 def cpu_baseline(w, q, k, v, budget_s=12.0):
     """The oracle as it stands, on a bounded sample of seeded query rows of the workload: with every BLAS
     thread, then (a smaller sample) with one."""
@@ -143,7 +160,9 @@ def run_workload(name, steps, warmup):
     fn = lambda: wan.wan_attn_fwd(q, k, v, out, w.batch, w.heads, w.s_q, w.s_kv, w.head_dim, w.path,
                                   stream)
     ms = time_calls(fn, steps, warmup, stream)
-    res = {"workload": name, "path": w.path, "ms": ms, "tflops": w.flops / (ms * 1e-3) / 1e12}
+    med, mn = step_stats(fn, steps, stream)
+    res = {"workload": name, "path": w.path, "ms": ms, "tflops": w.flops / (ms * 1e-3) / 1e12,
+           "ms_median": med, "ms_min": mn}
     res["frac_of_peak"] = res["tflops"] / PEAK_TFLOPS[w.path]
     kernel_ms = ms
     if w.path == "int8_fp8":
