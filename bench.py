@@ -322,11 +322,17 @@ def main():
     w, qkv, head, kernel_ms = run_workload(args.workload, args.steps, args.warmup)
     flops = w.flops
     achieved = flops / (kernel_ms * 1e-3) / 1e12
+    # secondary ceiling: one exponential per score, at the v_exp_f32 rate measured on gfx950 (28.4 lane
+    # results per clock per CU), 256 CUs at the nominal 2.4 GHz
+    exps = w.batch * w.heads * w.s_q * w.s_kv
+    exp_ms = exps / (28.4 * 256 * 2.4e9) * 1e3
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[w.path],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.path], 4),
             "traffic": measured_traffic(w.path, w.name),
             "kernel": "attn_fwd_bf16_kernel" if w.path == "bf16" else "attn8_fwd_kernel",
-            "flops_per_launch": flops}
+            "flops_per_launch": flops,
+            "exp_ceiling": {"exps_per_launch": exps, "ms_at_exp_rate": round(exp_ms, 3),
+                            "mfma_ms_at_peak": round(flops / (PEAK_TFLOPS[w.path] * 1e12) * 1e3, 3)}}
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(w, *qkv)
