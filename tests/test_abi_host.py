@@ -234,3 +234,18 @@ def test_vsa_scratch_bytes():
     ensure_built()
     assert wan.wan_vsa_select_scratch_bytes(2, 3, 150, 700) == 2 * 3 * (3 + 11) * 512
     assert wan.wan_vsa_select_scratch_bytes(0, 3, 150, 700) == 0
+
+
+def test_vsa_wrappers_reject_bad_tensors():
+    # the torch wrappers check device, dtype, layout and shapes before calling the library
+    import torch
+    q = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16)            # host tensors: not CUDA
+    idx = torch.zeros((1, 1, 1, 1), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        wan.vsa_select(q, q, 1)
+    with pytest.raises(ValueError):
+        wan.vsa_attention(q, q, q, idx)
+    with pytest.raises(ValueError):
+        wan.vsa_forward(q, q, q)
+    with pytest.raises(ValueError):
+        wan.vsa_select(q.float(), q, 1)                                  # wrong dtype
