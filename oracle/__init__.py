@@ -45,4 +45,4 @@ from .numerics import (  # noqa: F401
     int8_codes,
 )
 from .attn8 import attn8_emulate, attn8_quantize  # noqa: F401
-from .backward import attention_backward, lse_rows, dq_rows  # noqa: F401
+from .backward import attention_backward, lse_rows, dq_rows, dkdv_rows  # noqa: F401

@@ -22,6 +22,7 @@ the inputs; layouts are [b, s, H, d] for the tensors and [b, H, s_q] for lse.
 """
 
 import numpy as np
+import torch
 
 
 def _f64(x):
@@ -110,3 +111,51 @@ def dq_rows(q, k, v, do, rows):
         dd = (p * dp).sum(axis=1, keepdims=True)
         out[sel] = ((p * (dp - dd)) @ kk) * inv
     return out
+
+
+def _query_row_stats(qq, kk, vv, gg, inv, chunk=1024):
+    """lse_i and D_i = sum_j P_ij dP_ij of every query row of one head (float64 torch CPU tensors
+    qq, gg [s_q, d] and kk, vv [s_kv, d]), in chunks of query rows so that no full [s_q, s_kv]
+    matrix is held.  torch's CPU ops here only spread the elementwise work over the host's cores."""
+    s_q = qq.shape[0]
+    lse = torch.empty(s_q, dtype=torch.float64)
+    dd = torch.empty(s_q, dtype=torch.float64)
+    for i0 in range(0, s_q, chunk):
+        i1 = min(i0 + chunk, s_q)
+        s = (qq[i0:i1] @ kk.T) * inv
+        m = s.max(dim=1, keepdim=True).values
+        e = torch.exp(s - m)
+        l = e.sum(dim=1, keepdim=True)
+        dp = gg[i0:i1] @ vv.T
+        lse[i0:i1] = (m + torch.log(l))[:, 0]
+        dd[i0:i1] = ((e / l) * dp).sum(dim=1)
+    return lse, dd
+
+
+def dkdv_rows(q, k, v, do, rows):
+    """dK and dV for (batch, head, key index) triples -> (dk [n, d], dv [n, d]) float64.
+
+    Key row j of a head gathers over every query row i:  P_ij = exp(S_ij - lse_i),
+    dV_j = sum_i P_ij dO_i,  dS_ij = P_ij (dP_ij - D_i),  dK_j = sum_i dS_ij Q_i / sqrt(d),
+    with lse_i and D_i taken from the whole query row first (one pass over the head's keys per
+    head that the triples touch), so a few key rows cost about one forward of their heads."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
+    d = q.shape[-1]
+    out_k = np.empty((rows.shape[0], d))
+    out_v = np.empty((rows.shape[0], d))
+    if rows.shape[0] == 0:
+        return out_k, out_v
+    inv = 1.0 / np.sqrt(np.float64(d))
+    t64 = lambda x: torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    for bb, hh in np.unique(rows[:, :2], axis=0):
+        bb, hh = int(bb), int(hh)
+        sel = np.nonzero((rows[:, 0] == bb) & (rows[:, 1] == hh))[0]
+        qq, kk, vv, gg = (t64(x[bb, :, hh, :]) for x in (q, k, v, do))
+        lse, dd = _query_row_stats(qq, kk, vv, gg, inv)
+        j = torch.from_numpy(rows[sel, 2])
+        p = torch.exp((qq @ kk[j].T) * inv - lse[:, None])     # [s_q, n]: column j of P
+        dp = gg @ vv[j].T                                      # column j of dP
+        ds = p * (dp - dd[:, None])                            # column j of dS
+        out_v[sel] = (p.T @ gg).numpy()
+        out_k[sel] = ((ds.T @ qq) * inv).numpy()
+    return out_k, out_v

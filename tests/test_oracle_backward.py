@@ -147,3 +147,65 @@ def test_planted_mistakes_are_caught(monkeypatch, kind):
     monkeypatch.setattr(obw, "_head", _Mutant(kind))
     dq, dk, _, _ = obw.attention_backward(q, k, v, do)
     assert max(np.abs(dq - aq).max(), np.abs(dk - ak).max()) > 1e-6
+
+
+@pytest.mark.parametrize("b,H,s_q,s_kv,d", [(2, 3, 40, 30, 128), (1, 2, 129, 70, 128), (1, 1, 1, 5, 16),
+                                            (1, 1, 7, 1, 8)])
+def test_key_row_functions_match_full_and_autograd(b, H, s_q, s_kv, d):
+    q, k, v, do = _inputs(b, H, s_q, s_kv, d, 500 + s_q)
+    _, dk, dv, _ = oracle.attention_backward(q, k, v, do)
+    _, ak, av = _autograd(q, k, v, do)
+    rng = np.random.default_rng(501)
+    n = 12
+    rows = np.stack([rng.integers(0, b, n), rng.integers(0, H, n), rng.integers(0, s_kv, n)], 1)
+    rows[0] = [0, 0, 0]
+    rows[1] = [b - 1, H - 1, s_kv - 1]
+    gk, gv = oracle.dkdv_rows(q, k, v, do, rows)
+    for r, (bb, hh, j) in enumerate(rows):
+        assert np.allclose(gk[r], dk[bb, j, hh], rtol=1e-11, atol=1e-13)
+        assert np.allclose(gv[r], dv[bb, j, hh], rtol=1e-11, atol=1e-13)
+        assert np.allclose(gk[r], ak[bb, j, hh], rtol=1e-10, atol=1e-12)
+        assert np.allclose(gv[r], av[bb, j, hh], rtol=1e-10, atol=1e-12)
+    ek, ev = oracle.dkdv_rows(q, k, v, do, np.zeros((0, 3), np.int64))
+    assert ek.shape == (0, d) and ev.shape == (0, d)
+
+
+def test_key_row_statistics_chunks():
+    # the query-row statistics are taken in chunks of rows; a chunk boundary inside the head
+    # (and a partial last chunk) must not change them
+    q, k, v, do = _inputs(1, 1, 1100, 50, 32, 511)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x[0, :, 0, :], np.float64))
+    lse, dd = obw._query_row_stats(t(q), t(k), t(v), t(do), 1.0 / math.sqrt(32), chunk=512)
+    _, _, _, rlse = oracle.attention_backward(q, k, v, do)
+    assert np.allclose(lse.numpy(), rlse[0, 0], rtol=1e-13)
+    p = oracle.attention_probs(q, k, 0, 0, np.arange(1100))
+    dp = do[0, :, 0, :] @ v[0, :, 0, :].T
+    assert np.allclose(dd.numpy(), (p * dp).sum(axis=1), rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", ["lse_shift", "no_row_term", "no_scale"])
+def test_key_row_planted_mistakes_are_caught(monkeypatch, kind):
+    q, k, v, do = _inputs(1, 2, 20, 24, 16, 521, 1.5)
+    _, ak, av = _autograd(q, k, v, do)
+    rows = np.array([[0, h, j] for h in range(2) for j in range(24)])
+    orig = obw._query_row_stats
+    if kind == "lse_shift":        # P built from a wrong normaliser
+        monkeypatch.setattr(obw, "_query_row_stats", lambda *a, **kw: (orig(*a, **kw)[0] + 0.5, orig(*a, **kw)[1]))
+    elif kind == "no_row_term":    # dS without the softmax Jacobian's row term
+        monkeypatch.setattr(obw, "_query_row_stats", lambda *a, **kw: (orig(*a, **kw)[0], 0 * orig(*a, **kw)[1]))
+    else:                          # 1/sqrt(d) dropped everywhere
+        monkeypatch.setattr(obw, "np", _NumpyWithSqrt(lambda x: np.ones_like(np.asarray(x, np.float64))))
+    gk, gv = obw.dkdv_rows(q, k, v, do, rows)
+    ref_k = ak[0][rows[:, 2], rows[:, 1]]
+    ref_v = av[0][rows[:, 2], rows[:, 1]]
+    assert max(np.abs(gk - ref_k).max(), np.abs(gv - ref_v).max()) > 1e-6
+
+
+class _NumpyWithSqrt:
+    """numpy with sqrt replaced, to plant a mistake in the oracle."""
+
+    def __init__(self, sqrt):
+        self._sqrt = sqrt
+
+    def __getattr__(self, name):
+        return self._sqrt if name == "sqrt" else getattr(np, name)
