@@ -160,3 +160,38 @@ def test_planted_mistakes_are_caught(monkeypatch, mistake):
     monkeypatch.setattr(oatt, "np", _NumpyWithMistake(**mistake))
     bad = oatt.attention(q, k, v)
     assert np.max(np.abs(bad - ref)) > 1e-6
+
+
+def test_probabilities_brute_force():
+    q, k = _rand((1, 4, 2, 6), 111, 2.0), _rand((1, 9, 2, 6), 112, 2.0)
+    p = oracle.attention_probs(q, k, 0, 1, np.arange(4))
+    for i in range(4):
+        s = [math.fsum(float(q[0, i, 1, c]) * float(k[0, j, 1, c]) for c in range(6)) / math.sqrt(6)
+             for j in range(9)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        l = math.fsum(e)
+        for j in range(9):
+            assert abs(p[i, j] - e[j] / l) <= 1e-14
+
+
+def test_probabilities_times_values_give_the_output():
+    # P V is the attention output, which the brute-force and SDPA pins fix independently
+    q, k, v = _rand((2, 33, 3, 128), 121, 2.0), _rand((2, 70, 3, 128), 122, 2.0), _rand((2, 70, 3, 128), 123)
+    out = oracle.attention(q, k, v)
+    for bb, hh in ((0, 0), (1, 2)):
+        p = oracle.attention_probs(q, k, bb, hh, np.arange(33))
+        np.testing.assert_allclose(p @ v[bb, :, hh, :], out[bb, :, hh, :], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("mistake", [
+    dict(sqrt=lambda x: 1.0),                    # 1/sqrt(d) dropped
+    dict(sqrt=lambda x: x),                      # scale 1/d instead of 1/sqrt(d)
+    dict(exp=lambda x: np.exp2(x)),              # wrong exponential base
+])
+def test_probabilities_planted_mistakes_are_caught(monkeypatch, mistake):
+    q, k, v = _rand((1, 5, 1, 16), 131, 2.0), _rand((1, 7, 1, 16), 132, 2.0), _rand((1, 7, 1, 16), 133)
+    out = oracle.attention(q, k, v)          # taken before the mistake is planted
+    monkeypatch.setattr(oatt, "np", _NumpyWithMistake(**mistake))
+    bad = oatt.attention_probs(q, k, 0, 0, np.arange(5))
+    assert np.max(np.abs(bad @ v[0, :, 0, :] - out[0, :, 0, :])) > 1e-6

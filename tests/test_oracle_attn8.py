@@ -160,3 +160,93 @@ def test_planted_mistakes_are_caught(monkeypatch, where):
     rel, _ = _metrics(bad, ref)
     assert rel > 0.2
     del rng
+
+
+def _pow2_blocks(rng, s, d, exps, sigma=20.0):
+    """int8-exact operand with a distinct power-of-two scale per 64-token block: block i holds
+    integer codes (one of them 127, so the block maximum is 127 * 2^exps[i]) times 2^exps[i].  The
+    block quantisation then gives inv = 2^-exps[i], the codes themselves and scale 2^exps[i]."""
+    x = np.clip(np.rint(rng.standard_normal((s, d)) * sigma), -127, 127)
+    for i in range(-(-s // 64)):
+        x[64 * i, i % d] = 127
+        x[64 * i:64 * (i + 1)] *= 2.0 ** exps[i]
+    return x.astype(np.float32)
+
+
+def _exact_operand_case(seed):
+    """Q (150 tokens: blocks of 64, 64, 22) and K (300 tokens: 4 x 64 + 44) with distinct block
+    scales, V in e4m3 with every channel's maximum 448 (so its codes are exact with scale 1)."""
+    rng = np.random.default_rng(seed)
+    q = _pow2_blocks(rng, 150, 128, [-3, -6, -4])[None, :, None, :]
+    k = _pow2_blocks(rng, 300, 128, [-5, -2, -6, -3, -4])[None, :, None, :]
+    vv = oracle.e4m3fn_round(rng.standard_normal((1, 300, 1, 128)) * 60)
+    vv[0, 7, 0, :] = 448.0
+    return q, k, vv.astype(np.float32)
+
+
+def _exact_operand_bound(q, k, v, rows, ref, got):
+    """Per-element bound on |emulated - exact| when only P~ = e4m3(256 p) is rounded: each P~ is
+    within 2^-4 relative of 256 p (normal range) or 2^-10 absolute (subnormal), so
+    |O~ - O| <= (2^-4 sum_j p_j |v_j| + 2^-18 sum_j |v_j|) / l with exact p_j = exp(s_j - m) <= 1,
+    then half a bf16 ulp of the output."""
+    out = np.empty(ref.shape)
+    vv = np.abs(v[0, :, 0, :].astype(np.float64))
+    for r, (_, _, i) in enumerate(rows):
+        s = (q[0, i, 0, :].astype(np.float64) @ k[0, :, 0, :].astype(np.float64).T) / np.sqrt(128.0)
+        p = np.exp(s - s.max())
+        out[r] = (2.0 ** -4 * (p @ vv) + 2.0 ** -18 * vv.sum(axis=0)) / p.sum()
+    return out + 2.0 ** -8 * (np.abs(ref) + out)
+
+
+def test_exact_operands_with_distinct_block_scales():
+    q, k, v = _exact_operand_case(15)
+    rows = np.array([[0, 0, i] for i in range(150)])
+    z = attn8.attn8_quantize(q, k, v, smooth=False)[(0, 0)]
+    # the quantisation reproduces the codes and the power-of-two scales exactly
+    np.testing.assert_array_equal(z["q_scale"], 2.0 ** np.array([-3, -6, -4], np.float64))
+    np.testing.assert_array_equal(z["k_scale"], 2.0 ** np.array([-5, -2, -6, -3, -4], np.float64))
+    np.testing.assert_array_equal(z["q_codes"].astype(np.float64) * np.repeat(z["q_scale"], 64)[:150, None],
+                                  q[0, :, 0, :])
+    got = oracle.attn8_emulate(q, k, v, rows, smooth=False).astype(np.float64)
+    ref = oracle.attention_rows(q, k, v, rows)
+    bound = _exact_operand_bound(q, k, v, rows, ref, got)
+    assert np.all(np.abs(got - ref) <= bound)
+    assert np.mean(np.abs(got - ref)) < 0.25 * np.mean(bound)
+
+
+class _RollScales:
+    """attn8._block_int8 whose returned scales are shifted by one block on the n-th call of every
+    quantize_head (0: Q, 1: K): a block scale applied to the neighbouring block."""
+
+    def __init__(self, which):
+        self.which, self.calls, self.orig = which, 0, attn8._block_int8
+
+    def __call__(self, x, block):
+        codes, scales = self.orig(x, block)
+        hit = self.calls % 2 == self.which
+        self.calls += 1
+        return codes, (np.roll(scales, 1) if hit else scales)
+
+
+class _NumpyWithRepeat:
+    """numpy whose repeat is off by one token (the per-key scale expansion misaligned)."""
+
+    def __getattr__(self, name):
+        if name == "repeat":
+            return lambda a, r: np.roll(np.repeat(a, r), 1)
+        return getattr(np, name)
+
+
+@pytest.mark.parametrize("where", ["q_block_scale", "k_block_scale", "k_scale_token_shift"])
+def test_misaligned_block_scales_are_caught(monkeypatch, where):
+    q, k, v = _exact_operand_case(15)
+    rows = np.array([[0, 0, i] for i in range(150)])
+    ref = oracle.attention_rows(q, k, v, rows)
+    if where == "q_block_scale":
+        monkeypatch.setattr(attn8, "_block_int8", _RollScales(0))
+    elif where == "k_block_scale":
+        monkeypatch.setattr(attn8, "_block_int8", _RollScales(1))
+    else:
+        monkeypatch.setattr(attn8, "np", _NumpyWithRepeat())
+    bad = oracle.attn8_emulate(q, k, v, rows, smooth=False).astype(np.float64)
+    assert np.any(np.abs(bad - ref) > _exact_operand_bound(q, k, v, rows, ref, bad))
