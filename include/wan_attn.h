@@ -24,6 +24,12 @@
  * Errors: every function returns WAN_ATTN_OK (0) or a negative code below; it never aborts and
  * never prints unless the environment variable WAN_ATTN_LOG=1 is set.  Argument checks happen
  * before any work is enqueued, so a failed check leaves the stream untouched.
+ * Scratch memory: the entry points that need scratch take it from a per-device stream-ordered pool
+ * of the library (allocated and freed on the caller's stream).  Freed scratch stays in the pool
+ * for the next call (the largest call's scratch is kept for the life of the process) until
+ * wan_attn_release_scratch() returns it to the driver.  Test hook: if the environment variable
+ * WAN_ATTN_TEST_FAIL_ALLOC=1 is set when the library first needs scratch, every scratch
+ * allocation of the process fails with WAN_ATTN_ENOMEM (the variable is read once).
  */
 #ifndef WAN_ATTN_H
 #define WAN_ATTN_H
@@ -67,7 +73,8 @@ enum wan_attn_status {
  * parallel, and about batch*heads*ceil(s_q/256)*ranges*133 KB (ranges <= 2*CUs) of scratch is
  * allocated on `stream` and freed on `stream` after use.  int8_fp8: allocates about
  * s_q*heads*batch*(head_dim+4) + s_kv*heads*batch*(2*head_dim+4) bytes of scratch on `stream`,
- * freed on `stream` after use.  WAN_ATTN_ENOMEM when a scratch allocation fails.
+ * freed on `stream` after use.  WAN_ATTN_ENOMEM when a scratch allocation fails.  int8_fp8 also
+ * needs 128 * ceil(s_kv/64)*64 < 2^31 (s_kv up to 16,777,152; else WAN_ATTN_EUNSUPPORTED).
  */
 int wan_attn_fwd(const void* q, const void* k, const void* v, void* o,
                  int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv,
@@ -88,6 +95,7 @@ int wan_attn_fwd(const void* q, const void* k, const void* v, void* o,
  * codes 0, scale 1); V: one scale per channel over all tokens: inv = 448/amax,
  * code = e4m3(clamp(V*inv, +-448)) with round-to-nearest-even, scale = amax/448.
  * scratch must hold wan_attn8_quantize_scratch_bytes(batch, heads) bytes (16-byte aligned).
+ * No output (scratch included) may overlap another output or an input (WAN_ATTN_EINVAL).
  */
 int wan_attn8_quantize(const void* q, const void* k, const void* v,
                        int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim,
@@ -103,6 +111,8 @@ size_t wan_attn8_quantize_scratch_bytes(int64_t batch, int64_t heads);
  *   S = int32(q_code . k_code) * q_scale * k_scale / sqrt(128);  online softmax in fp32 over
  *   64-key blocks;  P~ = e4m3(p * 256);  O = alpha*O + P~ . V~ (fp8 MFMA, fp32 accumulation);
  *   l = alpha*l + sum p;  out = bf16(O * v_scale[c] / (256 * l)).
+ * o must not overlap the codes or scales (WAN_ATTN_EINVAL); 128 * ceil(s_kv/64)*64 < 2^31
+ * (WAN_ATTN_EUNSUPPORTED otherwise).
  */
 int wan_attn8_fwd_quantized(const void* q_codes, const void* q_scale,
                             const void* k_codes, const void* k_scale,
@@ -208,6 +218,12 @@ int wan_vsa_attn(const void* q, const void* k, const void* v, const void* block_
  * live in scratch allocated and freed on `stream` (WAN_ATTN_ENOMEM if that fails). */
 int wan_vsa_fwd(const void* q, const void* k, const void* v, void* o, int64_t batch, int64_t heads,
                 int64_t s_q, int64_t s_kv, int64_t head_dim, int64_t keep, void* stream);
+
+/* Returns the library's cached scratch memory (the pools of every device it has used) to the
+ * driver.  Call it when no call of the library is in flight on any stream (after synchronising
+ * them); later calls allocate scratch again.  WAN_ATTN_OK, or WAN_ATTN_ELAUNCH if the runtime
+ * refused. */
+int wan_attn_release_scratch(void);
 
 /* Static English text for a status code (never NULL). */
 const char* wan_attn_strerror(int code);

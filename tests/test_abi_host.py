@@ -249,3 +249,96 @@ def test_vsa_wrappers_reject_bad_tensors():
         wan.vsa_forward(q, q, q)
     with pytest.raises(ValueError):
         wan.vsa_select(q.float(), q, 1)                                  # wrong dtype
+
+
+def test_tensor_argument_helper_rejects_before_any_call():
+    # the check every torch wrapper applies to each tensor it hands to the library (out, lse,
+    # block_idx, FP8 codes and scales, the quantised operands): dtype, exact shape, contiguity,
+    # then CUDA device
+    import torch
+    cuda0 = torch.device("cuda", 0)
+    t = torch.zeros((2, 3, 4), dtype=torch.int32)
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        wan._require("block_idx", t, torch.int32, (2, 3, 4), cuda0)          # host memory
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        wan._require("lse", t.float(), torch.float32, (2, 3, 4), cuda0)       # host lse
+    with pytest.raises(ValueError, match="shape"):
+        wan._require("out", t, torch.int32, (2, 3, 5), cuda0)                 # undersized out
+    with pytest.raises(ValueError, match="uint8"):
+        wan._require("x_codes", t, torch.uint8, (2, 3, 4), cuda0)             # wrong dtype
+    with pytest.raises(ValueError, match="contiguous"):
+        wan._require("w_codes", t.transpose(0, 1), torch.int32, (3, 2, 4), cuda0)
+    with pytest.raises(ValueError, match="torch tensor"):
+        wan._require("x_scales", None, torch.float32, (1,), cuda0)
+
+
+def test_torch_wrappers_reject_host_tensors(monkeypatch):
+    # with host tensors every wrapper raises ValueError and never reaches the library
+    import torch
+
+    def no_library():
+        raise AssertionError("the library was called")
+
+    monkeypatch.setattr(wan, "lib", no_library)
+    q = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16)
+    lse = torch.zeros((1, 1, 64), dtype=torch.float32)
+    codes = torch.zeros((64, 64), dtype=torch.uint8)
+    scales = torch.ones((64,), dtype=torch.float32)
+    calls = [
+        lambda: wan.attention(q, q, q),
+        lambda: wan.attention_with_lse(q, q, q),
+        lambda: wan.attention_backward(q, q, q, q, lse, q),
+        lambda: wan.attention8_quantize(q, q, q),
+        lambda: wan.attention8_from_quantized({}, 1, 1, 64, 64),
+        lambda: wan.fp8_gemm(codes, scales, codes, scales[:1]),
+        lambda: wan.fp8_quantize_rows(q[0, :, 0, :]),
+        lambda: wan.fp8_quantize_tensor(q[0, :, 0, :]),
+        lambda: wan.vsa_attention(q, q, q, torch.zeros((1, 1, 1, 1), dtype=torch.int32)),
+    ]
+    for call in calls:
+        with pytest.raises(ValueError):
+            call()
+
+
+def test_attn8_key_length_limit():
+    # the 8-bit kernel's V-code descriptor spans 128 * ceil(s_kv/64)*64 bytes of one head: at 2^31 the
+    # call is refused before anything is enqueued (fake, far-apart addresses, never dereferenced)
+    lib = ensure_built()
+    q, k, v, o = 1 << 40, 1 << 41, 1 << 42, 1 << 43
+    assert lib.wan_attn_fwd(q, k, v, o, 1, 1, 1, 16777152 + 1, 128, 1, None) == wan.WAN_ATTN_EUNSUPPORTED
+    assert lib.wan_attn_fwd(q, k, v, o, 1, 1, 1, 1 << 24, 128, 1, None) == wan.WAN_ATTN_EUNSUPPORTED
+    assert lib.wan_attn8_fwd_quantized(q, q + (1 << 36), k, k + (1 << 36), v, v + (1 << 36), o, 1, 1, 1,
+                                       1 << 24, 128, None) == wan.WAN_ATTN_EUNSUPPORTED
+
+
+def _quantize_args(**kw):
+    """wan_attn8_quantize with distinct, far-apart fake addresses; every case fails a check first."""
+    names = ["q", "k", "v", "q_codes", "q_scale", "k_codes", "k_scale", "v_codes", "v_scale", "smooth", "scratch"]
+    a = {n: (i + 1) << 32 for i, n in enumerate(names)}
+    a.update(kw)
+    return [a["q"], a["k"], a["v"], 1, 2, 300, 257, 128] + [a[n] for n in names[3:]] + [None]
+
+
+@pytest.mark.parametrize("kw", [
+    dict(q_codes=1 << 32),                    # q codes over q
+    dict(k_scale=(2 << 32) + 4096),           # k scales inside k
+    dict(v_codes=6 << 32),                    # v codes over the q scales
+    dict(smooth=(9 << 32) + 256),             # smooth inside the v scales
+    dict(scratch=(4 << 32) + 64),             # scratch inside the q codes
+])
+def test_quantize_output_overlap(kw):
+    lib = ensure_built()
+    assert lib.wan_attn8_quantize(*_quantize_args(**kw)) == wan.WAN_ATTN_EINVAL
+
+
+@pytest.mark.parametrize("o", [1 << 32, (2 << 32) + 16, (5 << 32) + 4096, (6 << 32) + 16])
+def test_quantized_forward_output_overlap(o):
+    lib = ensure_built()
+    ptrs = [(i + 1) << 32 for i in range(6)]
+    assert lib.wan_attn8_fwd_quantized(*ptrs, o, 1, 2, 300, 257, 128, None) == wan.WAN_ATTN_EINVAL
+
+
+def test_release_scratch_without_pools():
+    # nothing allocated yet in this process: nothing to release
+    ensure_built()
+    assert wan.lib().wan_attn_release_scratch() == wan.WAN_ATTN_OK

@@ -56,6 +56,7 @@ _SIGNATURES = {
     "wan_vsa_select": (ctypes.c_int, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P]),
     "wan_vsa_attn": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_vsa_fwd": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_release_scratch": (ctypes.c_int, []),
     "wan_attn_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "wan_attn_version": (ctypes.c_int, []),
 }
@@ -107,6 +108,11 @@ def wan_attn_version():
     return lib().wan_attn_version()
 
 
+def wan_attn_release_scratch():
+    """Return the library's cached scratch memory to the driver (no call may be in flight)."""
+    _check(lib().wan_attn_release_scratch(), "wan_attn_release_scratch")
+
+
 def wan_attn_fwd(q, k, v, o, batch, heads, s_q, s_kv, head_dim, dtype, stream=None):
     dtype = DTYPES.get(dtype, dtype)
     rc = lib().wan_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), batch, heads, s_q, s_kv, head_dim,
@@ -147,14 +153,35 @@ def wan_attn8_fwd_quantized(q_codes, q_scale, k_codes, k_scale, v_codes, v_scale
     _check(rc, "wan_attn8_fwd_quantized")
 
 
+def _require(name, t, dtype, shape, device):
+    """Every tensor handed to the library: a contiguous tensor of ``dtype`` and exactly ``shape`` on
+    the CUDA device ``device`` (a wrong dtype or size, a strided view, host memory or another GPU
+    raise ValueError before any library call)."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device} (got {t.device})")
+    return t
+
+
 def _check_tensors(q, k, v):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 4:
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16 or not t.is_cuda
+                or not t.is_contiguous() or t.dim() != 4):
             raise ValueError(f"{name} must be a contiguous 4-d bfloat16 CUDA tensor [b, s, H, d]")
     b, s_q, H, d = q.shape
     if k.shape != v.shape or k.shape[0] != b or k.shape[2] != H or k.shape[3] != d:
         raise ValueError("k and v must be [b, s_kv, H, d] matching q [b, s_q, H, d]")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
     return b, H, s_q, k.shape[1], d
 
 
@@ -165,6 +192,7 @@ def attention(q, k, v, dtype="bf16", out=None, stream=None):
     b, H, s_q, s_kv, d = _check_tensors(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _require("out", out, torch.bfloat16, q.shape, q.device)
     wan_attn_fwd(q, k, v, out, b, H, s_q, s_kv, d, dtype, stream)
     return out
 
@@ -193,11 +221,24 @@ def attention8_quantize(q, k, v, stream=None):
     return out
 
 
+def _quantized_shapes(b, H, s_q, s_kv):
+    nbq = -(-s_q // QUANT_BLOCK)
+    nbk = -(-s_kv // QUANT_BLOCK)
+    import torch
+    return dict(q_codes=((b, s_q, H, HEAD_DIM), torch.int8), k_codes=((b, s_kv, H, HEAD_DIM), torch.int8),
+                q_scale=((b, H, nbq), torch.float32), k_scale=((b, H, nbk), torch.float32),
+                v_codes=((b, H, HEAD_DIM, nbk * QUANT_BLOCK), torch.uint8), v_scale=((b, H, HEAD_DIM), torch.float32))
+
+
 def attention8_from_quantized(z, b, H, s_q, s_kv, out=None, stream=None):
     """Stage 2 of the 8-bit path from the dict of ``attention8_quantize``."""
     import torch
+    dev = z["q_codes"].device if isinstance(z.get("q_codes"), torch.Tensor) else None
+    for name, (shape, dtype) in _quantized_shapes(b, H, s_q, s_kv).items():
+        _require(name, z.get(name), dtype, shape, dev)
     if out is None:
-        out = torch.empty((b, s_q, H, HEAD_DIM), dtype=torch.bfloat16, device=z["q_codes"].device)
+        out = torch.empty((b, s_q, H, HEAD_DIM), dtype=torch.bfloat16, device=dev)
+    _require("out", out, torch.bfloat16, (b, s_q, H, HEAD_DIM), dev)
     wan_attn8_fwd_quantized(z["q_codes"], z["q_scale"], z["k_codes"], z["k_scale"], z["v_codes"],
                             z["v_scale"], out, b, H, s_q, s_kv, HEAD_DIM, stream)
     return out
@@ -219,11 +260,9 @@ def attention_backward(q, k, v, o, lse, d_o, stream=None):
     output o and row log-sum-exp lse (attention_with_lse); new bfloat16 tensors."""
     import torch
     b, H, s_q, s_kv, d = _check_tensors(q, k, v)
-    for name, t, shape in (("o", o, q.shape), ("d_o", d_o, q.shape)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.shape != shape:
-            raise ValueError(f"{name} must be a contiguous bfloat16 CUDA tensor shaped like q")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or lse.shape != (b, H, s_q):
-        raise ValueError("lse must be a contiguous float32 tensor [b, H, s_q]")
+    _require("o", o, torch.bfloat16, q.shape, q.device)
+    _require("d_o", d_o, torch.bfloat16, q.shape, q.device)
+    _require("lse", lse, torch.float32, (b, H, s_q), q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, b, H, s_q, s_kv, d, stream)
     return dq, dk, dv
@@ -276,12 +315,20 @@ def fp8_gemm(x_codes, x_scales, w_codes, w_scale, out=None, stream=None):
     """y [m, n] bf16 = (x_codes [m, k] . w_codes [n, k]^T) * x_scales[m] * w_scale, from the codes and
     scales of fp8_quantize_rows / fp8_quantize_tensor."""
     import torch
+    if not isinstance(x_codes, torch.Tensor) or x_codes.dim() != 2:
+        raise ValueError("x_codes must be a 2-d uint8 CUDA tensor [m, k]")
+    if not isinstance(w_codes, torch.Tensor) or w_codes.dim() != 2:
+        raise ValueError("w_codes must be a 2-d uint8 CUDA tensor [n, k]")
     m, k = x_codes.shape
     n = w_codes.shape[0]
-    if w_codes.shape[1] != k or x_scales.numel() != m or w_scale.numel() != 1:
-        raise ValueError("shapes of codes and scales do not match")
+    dev = x_codes.device
+    _require("x_codes", x_codes, torch.uint8, (m, k), dev)
+    _require("w_codes", w_codes, torch.uint8, (n, k), dev)
+    _require("x_scales", x_scales, torch.float32, (m,), dev)
+    _require("w_scale", w_scale, torch.float32, (1,), dev)
     if out is None:
-        out = torch.empty((m, n), dtype=torch.bfloat16, device=x_codes.device)
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    _require("out", out, torch.bfloat16, (m, n), dev)
     wan_fp8_gemm(x_codes, x_scales, w_codes, w_scale, out, m, n, k, stream)
     return out
 
@@ -326,12 +373,14 @@ def vsa_select(q, k, keep=None, stream=None):
     """Coarse stage of block-sparse attention: the `keep` key blocks (64 tokens) of largest block score
     for every query block, block_idx [b, H, ceil(s_q/64), keep] int32 in ascending order."""
     import torch
-    b, s_q, H, d = q.shape
-    if k.dtype != torch.bfloat16 or not k.is_cuda or not k.is_contiguous() or k.dim() != 4 or k.shape[0] != b or k.shape[2] != H:
-        raise ValueError("k must be a contiguous bfloat16 tensor [b, s_kv, H, d] matching q")
-    if q.dtype != torch.bfloat16 or not q.is_cuda or not q.is_contiguous():
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a contiguous 4-d bfloat16 CUDA tensor [b, s, H, d]")
+    b, s_q, H, d = q.shape
+    _require("q", q, torch.bfloat16, q.shape, q.device)
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise ValueError("k must be a contiguous bfloat16 tensor [b, s_kv, H, d] matching q")
     s_kv = k.shape[1]
+    _require("k", k, torch.bfloat16, (b, s_kv, H, d), q.device)
     keep = vsa_default_keep(s_kv) if keep is None else keep
     idx = torch.empty((b, H, -(-s_q // VSA_BLOCK), keep), dtype=torch.int32, device=q.device)
     scratch = torch.empty(max(wan_vsa_select_scratch_bytes(b, H, s_q, s_kv), 16) // 4, dtype=torch.float32,
@@ -345,12 +394,14 @@ def vsa_attention(q, k, v, block_idx, out=None, stream=None):
     (block_idx [b, H, ceil(s_q/64), keep] int32); returns o [b, s_q, H, 128] bfloat16."""
     import torch
     b, H, s_q, s_kv, d = _check_tensors(q, k, v)
-    if (block_idx.dtype != torch.int32 or not block_idx.is_contiguous() or block_idx.dim() != 4
-            or tuple(block_idx.shape[:3]) != (b, H, -(-s_q // VSA_BLOCK))):
+    if not isinstance(block_idx, torch.Tensor) or block_idx.dim() != 4:
         raise ValueError("block_idx must be a contiguous int32 tensor [b, H, ceil(s_q/64), keep]")
+    keep = block_idx.shape[3]
+    _require("block_idx", block_idx, torch.int32, (b, H, -(-s_q // VSA_BLOCK), keep), q.device)
     if out is None:
         out = torch.empty_like(q)
-    wan_vsa_attn(q, k, v, block_idx, out, b, H, s_q, s_kv, d, block_idx.shape[3], stream)
+    _require("out", out, torch.bfloat16, q.shape, q.device)
+    wan_vsa_attn(q, k, v, block_idx, out, b, H, s_q, s_kv, d, keep, stream)
     return out
 
 
@@ -360,5 +411,6 @@ def vsa_forward(q, k, v, keep=None, out=None, stream=None):
     b, H, s_q, s_kv, d = _check_tensors(q, k, v)
     if out is None:
         out = torch.empty_like(q)
+    _require("out", out, torch.bfloat16, q.shape, q.device)
     wan_vsa_fwd(q, k, v, out, b, H, s_q, s_kv, d, 0 if keep is None else keep, stream)
     return out

@@ -51,6 +51,21 @@ int check_shape(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t
   return WAN_ATTN_OK;
 }
 
+// The first n_out buffers are outputs: none may overlap another output or any input.
+bool outputs_overlap(const void* const* ptrs, const int64_t* bytes, int n_out, int n) {
+  for (int a = 0; a < n_out; ++a)
+    for (int b = 0; b < n; ++b)
+      if (b != a && overlaps(ptrs[a], bytes[a], ptrs[b], bytes[b])) return true;
+  return false;
+}
+
+// The 8-bit kernel addresses a head's pre-transposed V codes (128 rows of s_kv_pad bytes) through
+// one buffer descriptor with a 32-bit byte range: 128 * s_kv_pad must stay below 2^31.
+int check_attn8_size(int64_t s_kv) {
+  const int64_t s_pad = wan::ceil_div(s_kv, wan::kQuantBlock) * wan::kQuantBlock;
+  return (int64_t)wan::kHeadDim * s_pad >= (1LL << 31) ? WAN_ATTN_EUNSUPPORTED : WAN_ATTN_OK;
+}
+
 int check_qkvo(const void* q, const void* k, const void* v, const void* o, int64_t batch,
                int64_t heads, int64_t s_q, int64_t s_kv) {
   if (!q || !k || !v || !o) return WAN_ATTN_EINVAL;
@@ -98,13 +113,23 @@ struct Attn8Layout {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Stream-ordered scratch from the device's pool (nullptr on failure; the test hook
-// WAN_ATTN_TEST_FAIL_ALLOC makes every allocation fail).
+// Test hook: with WAN_ATTN_TEST_FAIL_ALLOC=1 in the environment when the library first allocates
+// scratch, every scratch allocation of the process fails (WAN_ATTN_ENOMEM), so that callers can test
+// their handling of it.  Read once, like WAN_ATTN_LOG.
+bool fail_alloc_hook() {
+  static const bool on = [] {
+    const char* e = std::getenv("WAN_ATTN_TEST_FAIL_ALLOC");
+    return e != nullptr && e[0] == '1';
+  }();
+  return on;
+}
+
+// Stream-ordered scratch from the device's pool (nullptr on failure).
 void* scratch_alloc(size_t bytes, hipStream_t st, int* rc) {
   hipMemPool_t pool;
   *rc = pool_for_current_device(&pool);
   if (*rc) return nullptr;
-  if (std::getenv("WAN_ATTN_TEST_FAIL_ALLOC") != nullptr) {
+  if (fail_alloc_hook()) {
     *rc = WAN_ATTN_ENOMEM;
     return nullptr;
   }
@@ -180,6 +205,14 @@ extern "C" {
 
 int wan_attn_version(void) { return WAN_ATTN_VERSION; }
 
+int wan_attn_release_scratch(void) {
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  int rc = WAN_ATTN_OK;
+  for (hipMemPool_t pool : g_pools)
+    if (pool && hipMemPoolTrimTo(pool, 0) != hipSuccess) rc = WAN_ATTN_ELAUNCH;
+  return rc;
+}
+
 const char* wan_attn_strerror(int code) {
   switch (code) {
     case WAN_ATTN_OK: return "success";
@@ -206,9 +239,17 @@ int wan_attn8_quantize(const void* q, const void* k, const void* v, int64_t batc
   if (!q || !k || !v || !q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale ||
       !smooth || !scratch)
     return WAN_ATTN_EINVAL;
-  const void* ptrs[] = {q, k, v, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, smooth, scratch};
+  const void* ptrs[] = {q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, smooth, scratch, q, k, v};
   for (const void* p : ptrs)
     if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  {
+    const int64_t bh = batch * heads, d = wan::kHeadDim;
+    const int64_t nbq = wan::ceil_div(s_q, wan::kQuantBlock), nbk = wan::ceil_div(s_kv, wan::kQuantBlock);
+    const int64_t bytes[] = {bh * s_q * d, bh * nbq * 4, bh * s_kv * d, bh * nbk * 4, bh * d * nbk * wan::kQuantBlock,
+                             bh * d * 4, bh * d * 4, (int64_t)wan_attn8_quantize_scratch_bytes(batch, heads),
+                             bh * s_q * d * 2, bh * s_kv * d * 2, bh * s_kv * d * 2};
+    if (outputs_overlap(ptrs, bytes, 8, 11)) return WAN_ATTN_EINVAL;
+  }
   const wan::AttnShape sh{batch, heads, s_q, s_kv};
   WAN_LOG("quantize b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads,
           (long long)s_q, (long long)s_kv);
@@ -227,10 +268,19 @@ int wan_attn8_fwd_quantized(const void* q_codes, const void* q_scale, const void
                             int64_t head_dim, void* stream) {
   int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
   if (rc) return rc;
+  rc = check_attn8_size(s_kv);
+  if (rc) return rc;
   if (!q_codes || !q_scale || !k_codes || !k_scale || !v_codes || !v_scale || !o) return WAN_ATTN_EINVAL;
-  const void* ptrs[] = {q_codes, q_scale, k_codes, k_scale, v_codes, v_scale, o};
+  const void* ptrs[] = {o, q_codes, q_scale, k_codes, k_scale, v_codes, v_scale};
   for (const void* p : ptrs)
     if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  {
+    const int64_t bh = batch * heads, d = wan::kHeadDim;
+    const int64_t nbq = wan::ceil_div(s_q, wan::kQuantBlock), nbk = wan::ceil_div(s_kv, wan::kQuantBlock);
+    const int64_t bytes[] = {bh * s_q * d * 2, bh * s_q * d, bh * nbq * 4, bh * s_kv * d, bh * nbk * 4,
+                             bh * d * nbk * wan::kQuantBlock, bh * d * 4};
+    if (outputs_overlap(ptrs, bytes, 1, 7)) return WAN_ATTN_EINVAL;
+  }
   const wan::AttnShape sh{batch, heads, s_q, s_kv};
   return from_hip(wan::launch_attn8_fwd(static_cast<const int8_t*>(q_codes),
                                         static_cast<const float*>(q_scale),
@@ -248,6 +298,10 @@ int wan_attn_fwd(const void* q, const void* k, const void* v, void* o, int64_t b
   int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
   if (rc) return rc;
   if (dtype != WAN_ATTN_BF16 && dtype != WAN_ATTN_INT8_FP8) return WAN_ATTN_EINVAL;
+  if (dtype == WAN_ATTN_INT8_FP8) {
+    rc = check_attn8_size(s_kv);
+    if (rc) return rc;
+  }
   rc = check_qkvo(q, k, v, o, batch, heads, s_q, s_kv);
   if (rc) return rc;
   const wan::AttnShape sh{batch, heads, s_q, s_kv};
