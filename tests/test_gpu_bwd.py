@@ -2,9 +2,11 @@
 
 The forward that feeds it (wan_attn_fwd_lse) is checked first: its row log-sum-exp against the
 oracle's, its output against wan_attn_fwd's (bit for bit).  Gradients: small and ragged shapes
-compare every element of dQ, dK and dV with the oracle's exact gradients; a Wan-sized shape
-compares sampled dQ rows with the oracle and checks dK and dV through identities that hold at any
-size (sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
+compare every element of dQ, dK and dV with the oracle's exact gradients; the Wan-1.3B 480p and
+Wan-14B 720p shapes compare sampled dQ rows, and 64 sampled key rows of dK and dV per checked head
+(every head at 480p, two at 720p; each key row's gradient gathers every query row of its head), with
+the oracle, and check dK and dV over the whole tensors through identities that hold at any size
+(sum_j dK_j = 0, sum_j dV_j = sum_i dO_i).
 Bounds, per tensor over all checked elements: rel-L2 <= BWD_REL_L2 and max-abs <= BWD_MAX_REL times
 the largest magnitude of the exact gradient.
 """
@@ -89,14 +91,37 @@ def test_backward_batches_heads(b, H, s_q, s_kv):
     _full_case(b, H, s_q, s_kv, seed=b * 1000 + H * 100 + s_q)
 
 
-def test_backward_wan_sized():
-    # Wan2.1-1.3B at 480p, 81 frames: 12 heads x 32,760 tokens, one batch
+@pytest.fixture(scope="module")
+def wan13b_grads():
+    """Wan2.1-1.3B at 480p, 81 frames: 12 heads x 32,760 tokens, one batch entry."""
     b, H, s = 1, 12, 32760
     print(f"backward b={b} H={H} s={s}", flush=True)
     q, k, v, d_o = _inputs(b, H, s, s, 77)
     o, lse = wan.attention_with_lse(q, k, v)
     dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
     torch.cuda.synchronize()
+    return dict(q=q, k=k, v=v, d_o=d_o, dq=dq, dk=dk, dv=dv)
+
+
+@pytest.fixture(scope="module")
+def wan14b_grads():
+    """The backward the bench times: Wan-14B-shaped 720p, 81 frames, b=2, with the bench's own inputs
+    (make_qkv of the workload, dO from a generator seeded with the workload seed + 11)."""
+    w = wan_inputs.WORKLOADS["wan14b_720p81f_self"]
+    print(f"backward b={w.batch} H={w.heads} s={w.s_q}", flush=True)
+    q, k, v = wan_inputs.make_qkv(w, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
+    d_o = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    o, lse = wan.attention_with_lse(q, k, v)
+    dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
+    torch.cuda.synchronize()
+    return dict(q=q, k=k, v=v, d_o=d_o, dq=dq, dk=dk, dv=dv, w=w)
+
+
+def test_backward_wan_sized(wan13b_grads):
+    g = wan13b_grads
+    q, k, v, d_o, dq, dk, dv = (g[n] for n in ("q", "k", "v", "d_o", "dq", "dk", "dv"))
+    b, s, H, _ = q.shape
     rng = np.random.default_rng(78)
     rows = np.stack([np.zeros(48, np.int64), rng.integers(0, H, 48), rng.integers(0, s, 48)], 1)
     rows[0] = [0, 0, 0]
@@ -116,18 +141,43 @@ def test_backward_wan_sized():
     assert rel < 1e-2
 
 
-def test_backward_wan14b_720p_bench_inputs():
-    # the backward the bench times: Wan-14B-shaped 720p, 81 frames, b=2, with the bench's own inputs
-    # (make_qkv of the workload, dO from a generator seeded with the workload seed + 11)
-    w = wan_inputs.WORKLOADS["wan14b_720p81f_self"]
+def _key_rows(s, n, seed):
+    """n distinct key rows of a head, the first and the last among them."""
+    j = np.random.default_rng(seed).choice(np.arange(1, s - 1), n - 2, replace=False)
+    return np.sort(np.concatenate([[0, s - 1], j]))
+
+
+def _check_key_rows(g, pairs, n_rows, seed):
+    """dK and dV of sampled key rows of the (batch, head) pairs against the oracle's chain rule per key
+    row (every query row of the head enters each key row's gradient), on host copies of those heads."""
+    q, k, v, d_o, dk, dv = (g[n] for n in ("q", "k", "v", "d_o", "dk", "dv"))
+    s = k.shape[1]
+    got_k, got_v, ref_k, ref_v = [], [], [], []
+    for bb, hh in pairs:
+        head = [t[bb, :, hh, :].double().cpu().numpy()[None, :, None, :] for t in (q, k, v, d_o)]
+        j = _key_rows(s, n_rows, seed + 97 * bb + hh)
+        rows = np.stack([np.zeros_like(j), np.zeros_like(j), j], 1)
+        rk, rv = oracle.dkdv_rows(*head, rows)
+        ref_k.append(rk)
+        ref_v.append(rv)
+        got_k.append(dk[bb, torch.as_tensor(j, device=dk.device), hh, :].double().cpu().numpy())
+        got_v.append(dv[bb, torch.as_tensor(j, device=dv.device), hh, :].double().cpu().numpy())
+        print(f"  head (b={bb}, h={hh}): {len(j)} key rows", flush=True)
+    _check_grad("dk rows", np.concatenate(got_k), np.concatenate(ref_k))
+    _check_grad("dv rows", np.concatenate(got_v), np.concatenate(ref_v))
+
+
+@pytest.mark.parametrize("heads", [(0, 1, 2, 3), (4, 5, 6, 7), (8, 9, 10, 11)])
+def test_backward_wan_sized_key_rows(wan13b_grads, heads):
+    # 64 key rows (the first and last included) of every head, element by element
+    _check_key_rows(wan13b_grads, [(0, h) for h in heads], 64, 79)
+
+
+def test_backward_wan14b_720p_bench_inputs(wan14b_grads):
+    g = wan14b_grads
+    q, k, v, d_o, dq, dk, dv = (g[n] for n in ("q", "k", "v", "d_o", "dq", "dk", "dv"))
+    w = g["w"]
     b, H, s = w.batch, w.heads, w.s_q
-    print(f"backward b={b} H={H} s={s}", flush=True)
-    q, k, v = wan_inputs.make_qkv(w, device="cuda")
-    g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
-    d_o = torch.randn(q.shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
-    o, lse = wan.attention_with_lse(q, k, v)
-    dq, dk, dv = wan.attention_backward(q, k, v, o, lse, d_o)
-    torch.cuda.synchronize()
     # sampled dQ rows on 4 heads of both batch entries (the first and last rows among them), against
     # the oracle on host copies of those heads only
     heads = [0, 13, 27, H - 1]
@@ -148,3 +198,10 @@ def test_backward_wan14b_720p_bench_inputs():
     rel = float((dv.double().sum(dim=1) - d_o.double().sum(dim=1)).norm() / d_o.double().sum(dim=1).norm())
     print(f"  sum dK / sum |dK| max {ratio:.2e}, sum dV vs sum dO rel {rel:.2e}", flush=True)
     assert ratio < 2e-2 and rel < 1e-2
+
+
+@pytest.mark.parametrize("pair", [(0, 0), (1, 39)])
+def test_backward_wan14b_720p_key_rows(wan14b_grads, pair):
+    # 64 key rows (the first and last included) of the first head of batch entry 0 and the last head
+    # of batch entry 1, element by element
+    _check_key_rows(wan14b_grads, [pair], 64, 80)

@@ -188,3 +188,100 @@ def test_wan_projection_sampled(name):
     assert np.array_equal(wc_np, rwc) and _np(ws).view(np.uint32)[0] == np.float32(rws).view(np.uint32)
     _check_product(_f32(y[torch.as_tensor(rows, device="cuda")])[:16], xc_rows[:16], _np(xs)[rows][:16], wc_np,
                    _np(ws)[0])
+
+
+def _gemm_of_codes(xv, n=4):
+    """y = xv . 1^T through the library's GEMM: xv [m, 64] values that e4m3fn holds exactly, as codes
+    with scale 1; the weight rows are all 1.0 (code 0x38, scale 1), so every y[i, :] is the matrix core's
+    sum of the 64 products x[i, k] * 1 (one MFMA step), rounded to bf16."""
+    from oracle.numerics import e4m3fn_encode, e4m3fn_round
+    assert np.array_equal(e4m3fn_round(xv), xv)
+    m, k = xv.shape
+    xc = torch.tensor(e4m3fn_encode(xv), dtype=torch.uint8, device="cuda")
+    wc = torch.full((n, k), 0x38, dtype=torch.uint8, device="cuda")
+    ones_m = torch.ones((m,), dtype=torch.float32, device="cuda")
+    one = torch.ones((1,), dtype=torch.float32, device="cuda")
+    y = wan.fp8_gemm(xc, ones_m, wc, one)
+    torch.cuda.synchronize()
+    return _f32(y), _np(xc), _np(wc)
+
+
+def test_matrix_core_summation_window():
+    # The premise of the product bound above, measured through the GEMM: each group of 8 consecutive
+    # products is summed aligned to its largest product, bits below 2^-13 of that product's power of
+    # two dropped; products in other groups are summed exactly.  Cancelling large products in two
+    # groups leaves only the small ones, whose fate shows in the bf16 output.
+    xv = np.zeros((4, 64))
+    xv[0, 0], xv[0, 1:8], xv[0, 8] = 256.0, 2.0 ** -6, -256.0      # 2^-6 < 2^(8-13): dropped
+    xv[1, 0], xv[1, 1:8], xv[1, 8] = 256.0, 2.0 ** -5, -256.0      # 2^-5 = 2^(8-13): kept
+    xv[2, 0], xv[2, 8], xv[2, 16:24] = 256.0, -256.0, 2.0 ** -6    # small ones alone in group 2: exact
+    xv[3, 0], xv[3, 1:8], xv[3, 8] = 1.0, 2.0 ** -9, -1.0          # 2^-9 above 2^(0-13): kept
+    y, xc, wc = _gemm_of_codes(xv)
+    print("  sums:", y[:, 0], flush=True)
+    np.testing.assert_array_equal(y[:, 0], [0.0, 7 * 2.0 ** -5, 8 * 2.0 ** -6, 7 * 2.0 ** -9])
+    assert np.all(y == y[:, :1])
+    # the exact sums differ from row 0's result by the dropped products, which the bound covers
+    _check_product(y, xc, np.ones(4, np.float32), wc, np.float32(1.0))
+
+
+def test_summation_bound_on_adversarial_groups():
+    # in every row, each group of 8 products holds one large product +-2^e and seven small ones
+    # +-2^(e - gap) (random e, gap and signs); the large ones cancel in pairs of groups, so the output
+    # is the sum of the small products, which the summation window can truncate.  Every output must
+    # stay within the bound the parity tests use.
+    rng = np.random.default_rng(77)
+    m = 512
+    xv = np.zeros((m, 64))
+    for i in range(m):
+        for pair in range(4):
+            e = int(rng.integers(0, 9))
+            sign = float(rng.choice([-1.0, 1.0]))
+            for g, sg in ((2 * pair, sign), (2 * pair + 1, -sign)):
+                gap = int(rng.integers(3, 10 + e))           # small products down to 2^-9
+                xv[i, 8 * g] = sg * 2.0 ** e
+                xv[i, 8 * g + 1:8 * g + 8] = rng.choice([-1.0, 1.0], 7) * 2.0 ** (e - gap)
+    y, xc, wc = _gemm_of_codes(xv)
+    _check_product(y, xc, np.ones(m, np.float32), wc, np.float32(1.0))
+
+
+def _finite_bf16_up_to(limit):
+    """Every bf16 bit pattern whose value is finite with magnitude <= limit (both zeros included),
+    as float64 values."""
+    bits = np.arange(1 << 16, dtype=np.uint32) << 16
+    vals = bits.view(np.float32).astype(np.float64)
+    return vals[np.isfinite(vals) & (np.abs(vals) <= limit)]
+
+
+def test_every_bf16_value_converts_like_the_oracle():
+    # The device's e4m3fn conversion of every bf16 value it can be asked to convert (|x| <= 448 after the
+    # saturating clamp), through both quantisers: per-token activations with one 448 per row (scale 1,
+    # so the code is the conversion of x itself) and the 8-bit attention's V with one 448 per channel.
+    from oracle.numerics import e4m3fn_encode, e4m3fn_round
+    vals = _finite_bf16_up_to(448.0)
+    n = vals.size
+    print(f"  {n} bf16 values", flush=True)
+    cols = 1024
+    rows = -(-n // (cols - 1))
+    x = np.zeros((rows, cols))
+    x[:, 0] = 448.0
+    x.reshape(-1)[np.concatenate([np.arange(r * cols + 1, (r + 1) * cols) for r in range(rows)])[:n]] = vals
+    xt = torch.tensor(x, dtype=torch.float32).to(torch.bfloat16).cuda()
+    assert np.array_equal(_f32(xt).astype(np.float64), x)
+    xc, xs = wan.fp8_quantize_rows(xt)
+    torch.cuda.synchronize()
+    assert torch.all(xs == 1.0)
+    want = e4m3fn_encode(e4m3fn_round(x))
+    assert np.array_equal(_np(xc), want), int((_np(xc) != want).sum())
+
+    # V of one head: channel c holds 448 in token 0 and a slice of the values after it
+    s = 1 + -(-n // 128)
+    v = np.zeros((s, 128))
+    v[0, :] = 448.0
+    v[1:].reshape(-1)[:n] = vals
+    vt = torch.tensor(v, dtype=torch.float32).to(torch.bfloat16).cuda().reshape(1, s, 1, 128)
+    q = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16, device="cuda")
+    z = wan.attention8_quantize(q, vt, vt)             # zero Q: smoothing factors 1
+    torch.cuda.synchronize()
+    assert torch.all(z["v_scale"] == 1.0)
+    got = _np(z["v_codes"])[0, 0, :, :s].T                   # [s, 128]
+    assert np.array_equal(got, e4m3fn_encode(e4m3fn_round(v)))
