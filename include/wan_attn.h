@@ -152,6 +152,22 @@ int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
                  void* stream);
 
 /*
+ * wan_attn_bwd without any allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight training loops and harnesses that forbid hipMalloc.  Same arguments,
+ * checks and results (bit for bit) as wan_attn_bwd.  Instead of pool scratch it uses a static
+ * 64 MiB device array of the library (one per GPU, held until the process ends), so it needs
+ * 8 * batch * heads * ceil(s_q/64)*64 <= 64 MiB, i.e. batch * heads * ceil(s_q/64)*64 <= 8,388,608
+ * (Wan-14B 720p at batch 2 and 40 heads: 6,051,840), else WAN_ATTN_EUNSUPPORTED.  Its first call on
+ * a device looks up that device's copy of the array.  Every call on one GPU shares the array: calls
+ * that overlap in time on one GPU (on different streams, or from different threads) race and give
+ * wrong gradients; calls ordered on one stream do not.  No state carries from one call to the next.
+ */
+int wan_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                         const void* lse, void* dq, void* dk, void* dv,
+                         int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t head_dim,
+                         void* stream);
+
+/*
  * FP8 GEMM of the DiT linear layers (the alpha term of the cost model): Y = X W^T in FP8 with the
  * activations quantised per token and the weights per tensor ("Wan模型是什么它能做什么"
  * explainer, section 4.2, where every matrix multiplication of the linear layers runs this way).

@@ -342,3 +342,21 @@ def test_release_scratch_without_pools():
     # nothing allocated yet in this process: nothing to release
     ensure_built()
     assert wan.lib().wan_attn_release_scratch() == wan.WAN_ATTN_OK
+
+
+def test_noalloc_backward_size_limit():
+    # the static scratch holds 8 bytes per padded query row, 64 MiB: 8,388,608 rows; one tile more is
+    # refused before any GPU work (fake, far-apart addresses, never dereferenced)
+    lib = ensure_built()
+    names = ["q", "k", "v", "o", "d_o", "lse", "dq", "dk", "dv"]
+    ptrs = [(i + 1) << 40 for i in range(len(names))]
+    assert lib.wan_attn_bwd_noalloc(*ptrs, 1, 1, 8388608 + 64, 1, 128, None) == wan.WAN_ATTN_EUNSUPPORTED
+    assert lib.wan_attn_bwd_noalloc(*ptrs, 2, 64, 65537, 1, 128, None) == wan.WAN_ATTN_EUNSUPPORTED
+    # the other checks are the allocating backward's
+    bad = list(ptrs)
+    bad[6] = ptrs[0]                      # dq over q
+    assert lib.wan_attn_bwd_noalloc(*bad, 1, 1, 64, 64, 128, None) == wan.WAN_ATTN_EINVAL
+    bad = list(ptrs)
+    bad[5] = None
+    assert lib.wan_attn_bwd_noalloc(*bad, 1, 1, 64, 64, 128, None) == wan.WAN_ATTN_EINVAL
+    assert lib.wan_attn_bwd_noalloc(*ptrs, 1, 1, 64, 64, 64, None) == wan.WAN_ATTN_EUNSUPPORTED

@@ -49,6 +49,7 @@ _SIGNATURES = {
                                                _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_fwd_lse": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    "wan_attn_bwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     "wan_fp8_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "wan_fp8_quantize_tensor": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "wan_fp8_gemm": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -130,6 +131,12 @@ def wan_attn_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, s_q, s_kv, head
     rc = lib().wan_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
                             _ptr(dv), batch, heads, s_q, s_kv, head_dim, _stream(stream))
     _check(rc, "wan_attn_bwd")
+
+
+def wan_attn_bwd_noalloc(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, s_q, s_kv, head_dim, stream=None):
+    rc = lib().wan_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(d_o), _ptr(lse), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), batch, heads, s_q, s_kv, head_dim, _stream(stream))
+    _check(rc, "wan_attn_bwd_noalloc")
 
 
 def wan_attn8_quantize_scratch_bytes(batch, heads):

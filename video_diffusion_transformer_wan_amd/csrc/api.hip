@@ -198,6 +198,54 @@ int check_vsa(int64_t batch, int64_t heads, int64_t s_q, int64_t s_kv, int64_t k
   return WAN_ATTN_OK;
 }
 
+// Argument checks of the backward entry points: sizes, null and alignment, and no output overlapping
+// an input or another output.
+int check_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o, const void* lse,
+              const void* dq, const void* dk, const void* dv, int64_t batch, int64_t heads, int64_t s_q,
+              int64_t s_kv, int64_t head_dim) {
+  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  const void* ptrs[] = {dq, dk, dv, q, k, v, o, d_o, lse};
+  for (const void* p : ptrs)
+    if (!p) return WAN_ATTN_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return WAN_ATTN_EALIGN;
+  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
+  const int64_t kb = batch * s_kv * heads * wan::kHeadDim * 2;
+  const int64_t lb = batch * heads * s_q * 4;
+  const int64_t bytes[] = {qb, kb, kb, qb, kb, kb, qb, qb, lb};
+  if (outputs_overlap(ptrs, bytes, 3, 9)) return WAN_ATTN_EINVAL;
+  return WAN_ATTN_OK;
+}
+
+// Scratch of wan_attn_bwd_noalloc, for callers that cannot allocate: the backward's per-row
+// statistics (lse * log2(e) and D, 8 bytes per query row padded to 64) in a file-scope device array.
+// Every GPU the library runs on holds its own copy until the process ends.  In host code the array's
+// name is only a host-side stand-in: the kernels get the address that hipGetSymbolAddress returns for
+// the current device, looked up once per device on that device's first call.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[64] = {};
+
+int noalloc_scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return WAN_ATTN_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      WAN_LOG("hipGetSymbolAddress of the no-allocation scratch failed: %s", hipGetErrorString(e));
+      return WAN_ATTN_ELAUNCH;
+    }
+    g_noalloc_ptr[dev] = ptr;
+  }
+  *out = g_noalloc_ptr[dev];
+  return WAN_ATTN_OK;
+}
+
 }  // namespace
 
 
@@ -355,26 +403,8 @@ int wan_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, void*
 int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* d_o,
                  const void* lse, void* dq, void* dk, void* dv, int64_t batch, int64_t heads,
                  int64_t s_q, int64_t s_kv, int64_t head_dim, void* stream) {
-  int rc = check_shape(batch, heads, s_q, s_kv, head_dim);
+  int rc = check_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, s_q, s_kv, head_dim);
   if (rc) return rc;
-  const void* ptrs[] = {q, k, v, o, d_o, lse, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!p) return WAN_ATTN_EINVAL;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return WAN_ATTN_EALIGN;
-  const int64_t qb = batch * s_q * heads * wan::kHeadDim * 2;
-  const int64_t kb = batch * s_kv * heads * wan::kHeadDim * 2;
-  const int64_t lb = batch * heads * s_q * 4;
-  const void* ins[] = {q, k, v, o, d_o, lse};
-  const int64_t in_bytes[] = {qb, kb, kb, qb, qb, lb};
-  void* outs[] = {dq, dk, dv};
-  const int64_t out_bytes[] = {qb, kb, kb};
-  for (int a = 0; a < 3; ++a) {
-    for (int b = 0; b < 6; ++b)
-      if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return WAN_ATTN_EINVAL;
-    for (int b = a + 1; b < 3; ++b)
-      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return WAN_ATTN_EINVAL;
-  }
   const wan::AttnShape sh{batch, heads, s_q, s_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   WAN_LOG("bwd b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads, (long long)s_q,
@@ -386,6 +416,27 @@ int wan_attn_bwd(const void* q, const void* k, const void* v, const void* o, con
   hipError_t fe = hipFreeAsync(ws, st);
   if (!rc && fe != hipSuccess) rc = from_hip(fe, "scratch release");
   return rc;
+}
+
+int wan_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* d_o,
+                         const void* lse, void* dq, void* dk, void* dv, int64_t batch, int64_t heads,
+                         int64_t s_q, int64_t s_kv, int64_t head_dim, void* stream) {
+  int rc = check_bwd(q, k, v, o, d_o, lse, dq, dk, dv, batch, heads, s_q, s_kv, head_dim);
+  if (rc) return rc;
+  const wan::AttnShape sh{batch, heads, s_q, s_kv};
+  if (wan::attn_bwd_scratch_bytes(sh) > kNoallocScratchBytes) {
+    WAN_LOG("bwd_noalloc: %zu bytes of row statistics exceed the %zu-byte static scratch",
+            wan::attn_bwd_scratch_bytes(sh), kNoallocScratchBytes);
+    return WAN_ATTN_EUNSUPPORTED;
+  }
+  void* ws = nullptr;
+  rc = noalloc_scratch_for_current_device(&ws);
+  if (rc) return rc;
+  WAN_LOG("bwd_noalloc b=%lld H=%lld s_q=%lld s_kv=%lld", (long long)batch, (long long)heads, (long long)s_q,
+          (long long)s_kv);
+  return from_hip(wan::launch_attn_bwd(q, k, v, o, d_o, static_cast<const float*>(lse), dq, dk, dv, sh, ws,
+                                       static_cast<hipStream_t>(stream)),
+                  "backward launch");
 }
 
 int wan_fp8_quantize_rows(const void* x, int64_t rows, int64_t cols, void* codes, void* scales, void* stream) {
