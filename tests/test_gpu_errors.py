@@ -117,7 +117,8 @@ def test_wrappers_reject_bad_tensor_arguments(monkeypatch):
         "host lse": lambda: wan.attention_backward(q, k, v, o, lse.cpu(), o),
         "short lse": lambda: wan.attention_backward(q, k, v, o, lse[:, :, :-1].contiguous(), o),
         "undersized out": lambda: wan.attention(q, k, v, out=torch.empty_like(q)[:, :-1]),
-        "strided out": lambda: wan.attention(q, k, v, out=torch.empty_like(q.transpose(1, 2)).transpose(1, 2)),
+        "strided out": lambda: wan.attention(q, k, v, out=torch.empty((1, 2, 130, 128), dtype=torch.bfloat16,
+                                                                       device="cuda").transpose(1, 2)),
         "fp32 out": lambda: wan.vsa_forward(q, k, v, out=torch.empty(q.shape, device="cuda")),
         "host fp8 codes": lambda: wan.fp8_gemm(codes.cpu(), scales, wcodes, wscale),
         "host fp8 scales": lambda: wan.fp8_gemm(codes, scales.cpu(), wcodes, wscale),

@@ -248,7 +248,8 @@ def _finite_bf16_up_to(limit):
     """Every bf16 bit pattern whose value is finite with magnitude <= limit (both zeros included),
     as float64 values."""
     bits = np.arange(1 << 16, dtype=np.uint32) << 16
-    vals = bits.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        vals = bits.view(np.float32).astype(np.float64)
     return vals[np.isfinite(vals) & (np.abs(vals) <= limit)]
 
 
