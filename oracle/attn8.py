@@ -19,8 +19,11 @@ the 8-bit GPU path, which is written separately):
   5. m' = max(m, row max of S); alpha = exp(m - m'); p = exp(S - m').
   6. P~ = e4m3fn(p * 2^8): the power-of-two factor keeps p in the normal range of e4m3fn and is
      removed again at the end.
-  7. O = alpha * O + P~ . V~ ; l = alpha * l + sum p (the row sum uses p before FP8 rounding).
-  8. Out = bf16(O * scale_v[c] / (2^8 * l)).
+  7. O = alpha * O + P~ . V~ ; l = alpha * l + sum P~ (the row sum adds the same FP8 weights that
+     multiply V, so the output is a weighted mean whose weights sum to one; the pages fix only that
+     the accumulation across KV blocks is FP32, not whether the normaliser uses P before or after
+     its FP8 rounding).
+  8. Out = bf16(O * scale_v[c] / l)   (l carries the factor 2^8 of P~).
 
 Quantisation decisions (steps 1-3) are taken in float32, as the GPU path takes them, so that the
 int8 and e4m3 codes can be compared bit for bit.  Steps 4-8 run in float64: this emulator is a
@@ -120,10 +123,10 @@ def _attend_head(qz, qi, kv_block, block):
         a = np.exp(m - m_new)
         p = np.exp(S - m_new[:, None])
         pt = e4m3fn_round(p * 256.0)
-        l = a * l + p.sum(axis=1)
+        l = a * l + pt.sum(axis=1)
         o = a[:, None] * o + pt @ vt[j0:j1]
         m = m_new
-    out = (o * qz["v_scale"].astype(np.float64)[None, :]) / (256.0 * l[:, None])
+    out = (o * qz["v_scale"].astype(np.float64)[None, :]) / l[:, None]
     return bf16_round(out.astype(F32))
 
 

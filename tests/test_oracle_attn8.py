@@ -4,8 +4,12 @@
   block maximum maps to +-127, every e4m3 value is within the format's relative half-step of
   V * inv, the channel maximum maps to +-448; exactly representable inputs round-trip exactly.
 * Smoothing balances the per-channel maxima of Q' and K' and leaves QK^T unchanged (fp64 check).
-* Special cases that reduce to the exact attention: one key returns its V row; with exactly
-  representable operands the only error left is the FP8 rounding of P, bounded by 2^-4 * max|V|.
+* Special cases that reduce to the exact attention: one key returns its V row; a V that is the same
+  in every key returns it exactly (the normaliser sums the same FP8 weights that multiply V); with
+  exactly representable operands -- also with a distinct power-of-two scale in every Q and K block --
+  the only error left is the FP8 rounding of P, within a bound derived from e4m3's half step; planted
+  mistakes (a dropped P or V scale, block scales shifted by a block or a token, the normaliser taken
+  from P before its FP8 rounding) break these pins.
 * The 8-bit path's accuracy bounds (rel-L2 <= 6e-2, cosine >= 0.995 against exact attention) on
   a small seeded workload with 1% outlier channels at 8 sigma, and that the literal scheme without
   smoothing is worse there.
@@ -107,10 +111,10 @@ def test_exact_operands_leave_only_fp8_rounding_of_p():
     rows = np.array([[0, 0, i] for i in range(64)])
     got = oracle.attn8_emulate(q, k, v, rows, smooth=False).astype(np.float64)
     ref = oracle.attention_rows(q, k, v, rows)
-    bound = 2 ** -4 * np.abs(v).max() + 2 ** -8 * np.abs(ref)
+    bound = _exact_operand_bound(q, k, v, rows, ref, got)
     assert np.all(np.abs(got - ref) <= bound)
     # and the bound is not trivially loose: the mean error is far below it
-    assert np.mean(np.abs(got - ref)) < 0.1 * 2 ** -4 * np.abs(v).max()
+    assert np.mean(np.abs(got - ref)) < 0.25 * np.mean(bound)
 
 
 def _outlier_case(seed, H=4, s=8192, d=128, n_rows=48):
@@ -185,16 +189,18 @@ def _exact_operand_case(seed):
 
 
 def _exact_operand_bound(q, k, v, rows, ref, got):
-    """Per-element bound on |emulated - exact| when only P~ = e4m3(256 p) is rounded: each P~ is
-    within 2^-4 relative of 256 p (normal range) or 2^-10 absolute (subnormal), so
-    |O~ - O| <= (2^-4 sum_j p_j |v_j| + 2^-18 sum_j |v_j|) / l with exact p_j = exp(s_j - m) <= 1,
-    then half a bf16 ulp of the output."""
+    """Per-element bound on |emulated - exact| when only P~ = e4m3(256 p) is rounded.  With
+    P~_j = 256 p_j + delta_j, |delta_j| <= max(2^-4 * 256 p_j, 2^-10) (half a step of e4m3fn in its
+    normal and subnormal range), L = sum_j p_j and O the exact output row, the emulator's
+    sum_j P~_j V_j / sum_j P~_j differs from O by sum_j delta_j (V_j - O) / sum_j P~_j, so
+    |O~ - O| <= sum_j |delta_j| |V_j - O| / (256 L - sum_j |delta_j|); then half a bf16 ulp."""
     out = np.empty(ref.shape)
-    vv = np.abs(v[0, :, 0, :].astype(np.float64))
+    vv = v[0, :, 0, :].astype(np.float64)
     for r, (_, _, i) in enumerate(rows):
         s = (q[0, i, 0, :].astype(np.float64) @ k[0, :, 0, :].astype(np.float64).T) / np.sqrt(128.0)
         p = np.exp(s - s.max())
-        out[r] = (2.0 ** -4 * (p @ vv) + 2.0 ** -18 * vv.sum(axis=0)) / p.sum()
+        dlt = np.maximum(2.0 ** -4 * 256.0 * p, 2.0 ** -10)
+        out[r] = (dlt @ np.abs(vv - ref[r][None, :])) / (256.0 * p.sum() - dlt.sum())
     return out + 2.0 ** -8 * (np.abs(ref) + out)
 
 
@@ -250,3 +256,39 @@ def test_misaligned_block_scales_are_caught(monkeypatch, where):
         monkeypatch.setattr(attn8, "np", _NumpyWithRepeat())
     bad = oracle.attn8_emulate(q, k, v, rows, smooth=False).astype(np.float64)
     assert np.any(np.abs(bad - ref) > _exact_operand_bound(q, k, v, rows, ref, bad))
+
+
+def _uniform_v_case():
+    q = _gauss((1, 70, 2, 128), 31, 2.0)
+    k = _gauss((1, 300, 2, 128), 32, 2.0)
+    row = _bf16(np.random.default_rng(33).standard_normal(128) * 3)
+    v = np.broadcast_to(row, (1, 300, 2, 128)).astype(np.float32).copy()
+    rows = np.array([[0, h, i] for h in range(2) for i in range(70)])
+    return q, k, v, row, rows
+
+
+def test_uniform_values_return_that_row_exactly():
+    # every key's V row equal: sum_j P~_j v / sum_j P~_j = v whatever the weights
+    q, k, v, row, rows = _uniform_v_case()
+    got = oracle.attn8_emulate(q, k, v, rows)
+    np.testing.assert_array_equal(got, np.broadcast_to(row, got.shape))
+
+
+def test_normaliser_before_rounding_is_caught(monkeypatch):
+    # the other reading (l from p before its FP8 rounding) breaks the uniform-V pin
+    q, k, v, row, rows = _uniform_v_case()
+    def old_normaliser(qz, qi, kv_block, block):
+        qc = qz["q_codes"][qi].astype(np.float64)
+        sq = qz["q_scale"][qi // block].astype(np.float64)
+        kc = qz["k_codes"].astype(np.float64)
+        sk = np.repeat(qz["k_scale"].astype(np.float64), block)[:kc.shape[0]]
+        vt = oracle.e4m3fn_decode(qz["v_codes"])
+        s = (qc @ kc.T) * sq[:, None] * sk[None, :] / np.sqrt(128.0)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        pt = oracle.e4m3fn_round(p * 256.0)
+        out = (pt @ vt) * qz["v_scale"].astype(np.float64)[None, :] / (256.0 * p.sum(axis=1)[:, None])
+        return oracle.bf16_round(out.astype(np.float32))
+
+    monkeypatch.setattr(attn8, "_attend_head", old_normaliser)
+    bad = oracle.attn8_emulate(q, k, v, rows)
+    assert not np.array_equal(bad, np.broadcast_to(row, bad.shape))

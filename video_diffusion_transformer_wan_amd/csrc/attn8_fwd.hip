@@ -6,7 +6,10 @@
 //   S   = int32(q_code . k_code) * q_scale * k_scale / sqrt(128)        (v_mfma_i32_32x32x32_i8)
 //   m'  = max(m, row max S);  alpha = exp(m - m');  p = exp(S - m')    (fp32)
 //   P~  = e4m3(p * 2^8);  O = alpha*O + P~ . V~ (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulators)
-//   l   = alpha*l + sum p;  out = bf16(O * v_scale[c] / (2^8 * l))
+//   l   = alpha*l + sum P~;  out = bf16(O * v_scale[c] / l)     (l carries the 2^8 of P~)
+// The normaliser sums the same FP8 weights that multiply V (the pages fix FP32 accumulation across
+// KV blocks, not which P the normaliser adds), so it runs on the matrix core too: one more fp8 MFMA
+// per tile with an all-ones A operand gives every query's sum of P~ over the tile's 64 keys.
 // The running max moves whenever a row's max grows (p * 2^8 <= 256 stays inside e4m3's range).
 //
 // Design (the bf16 kernel's, with 8-bit operands): one workgroup = 8 waves = 256 query rows of
@@ -136,6 +139,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
                     kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
                     kMagicBits, kMagicBits, kMagicBits, kMagicBits};
   asm volatile("" : "+v"(magic));
+  // A operand of the row-sum MFMA: 32 rows x 64 keys of e4m3 1.0 (code 0x38)
+  i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                  0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  asm volatile("" : "+v"(ones));
 
   // Persistent, XCD-aware: workgroup w runs on XCD w % 8 and takes query tiles slot, slot +
   // n_slots, ... of that XCD's contiguous range, so the workgroups of one XCD sweep consecutive
@@ -168,18 +175,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
     for (int c = 0; c < 4; ++c)
       qf[c] = *reinterpret_cast<const i32x4_t*>(qbase + (int64_t)q_rc * tok_stride + 32 * c + 16 * h);
     const float q_scale = p.qs[(int64_t)bh * p.nbq + q_rc / kBN];
-    // v_scale of the lane's output channels 32db + 8g + 4h .. +3, fetched now for the epilogue
-    float vsv[4][4][4];
-    {
-      const float* vsc = p.vs + (int64_t)bh * kHeadDim + 4 * h;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vsv[db][g][e] = vsc[32 * db + 8 * g + e];
-    }
-
     auto issue_tile = [&](int j) __attribute__((always_inline)) {
       const int kv0 = j * kBN;
       const __amdgpu_buffer_rsrc_t kr =
@@ -196,7 +191,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m = kNeg;     // running max of S in log2 units
-    float l = 0.0f;     // lane's part of the running sum of p * 2^8
+    // running sum of P~ (= p * 2^8 in FP8) per query: every register of the row-sum MFMA's output holds
+    // the query's sum; only register 0 is read (and rescaled), the others are left unscaled.
+    f32x16_t lsum;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) lsum[r] = 0.0f;
     i32x16_t s[2];      // S^T of the newest tile per 32-key block, as 1.5 * 2^23 + integer sum
     unsigned pb[8];     // P~ of the tile awaiting its PV product: bytes 16kb + r <-> s[kb][r]
 
@@ -209,6 +208,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
       const unsigned char* ks = smem + (j % kStages) * kStageBytes;
       const unsigned char* vts = smem + ((j + kStages - 1) % kStages) * kStageBytes + kKBytes;
       __builtin_amdgcn_s_setprio(3);
+      if constexpr (kPV) {
+        const i32x8_t bop = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3],
+                             (int)pb[4], (int)pb[5], (int)pb[6], (int)pb[7]};
+        lsum = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, bop, lsum, 0, 0, 0, 0, 0, 0);
+      }
       constexpr int kFirst = kQK ? 0 : 4;
       constexpr int kSteps = kPV ? 8 : 4;
       i32x4_t ring[2][2];
@@ -278,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
       if (__any(mnew > m)) {
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         m = mnew;
-        l *= alpha;
+        lsum[0] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -295,7 +299,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
           const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[kb][r + 1], f, bias));
           const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[kb][r + 2], f, bias));
           const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sf[kb][r + 3], f, bias));
-          l += (p0 + p1) + (p2 + p3);
           // both halves of the word are written, so the old value passed in is never kept (a
           // constant there would cost a v_mov per word)
           int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, (int)pb[4 * kb + wd], false);
@@ -332,12 +335,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
     if (first_group) barrier();
     barrier();   // every wave is done with the LDS ring before the next tile's loads
 
-    // ---- epilogue: out = O * v_scale[c] / l  (l carries the 2^8 of P~)
-    float la, lb;
-    pair_values(l, la, lb);
-    const float inv = 1.0f / (la + lb);
+    // ---- epilogue: out = O * v_scale[c] / l  (l carries the 2^8 of P~); the lane's output
+    // channels are 32db + 8g + 4h .. +3
+    const float inv = 1.0f / lsum[0];
     if (q_row < p.s_q) {
       uint16_t* dst = obase + (int64_t)q_row * tok_stride + 4 * h;
+      const float* vsc = p.vs + (int64_t)bh * kHeadDim + 4 * h;
+      float vsv[4][4][4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vsv[db][g][e] = vsc[32 * db + 8 * g + e];
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
