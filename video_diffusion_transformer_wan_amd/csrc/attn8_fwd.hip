@@ -58,6 +58,7 @@ constexpr float kMagic = 12582912.0f;     // 1.5 * 2^23
 constexpr float kNeg = -1.0e30f;          // masked score (finite: keeps inf - inf out)
 constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
 constexpr short kWaitVm0 = 0x0F70;             // s_waitcnt vmcnt(0), other counters untouched
+constexpr short kWaitVm2 = 0x0F72;             // s_waitcnt vmcnt(2): one tile's two loads may stay in flight
 
 struct Params {
   const int8_t* qc;
@@ -207,6 +208,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
       constexpr bool kPV = decltype(pv_tag)::value;
       const unsigned char* ks = smem + (j % kStages) * kStageBytes;
       const unsigned char* vts = smem + ((j + kStages - 1) % kStages) * kStageBytes + kKBytes;
+      // this wave's share of the loads of tile j+2: its descriptor arithmetic is scalar work that
+      // would otherwise sit on the softmax half-step's critical path
+      const bool load_next = kQK && j + 2 < n_tiles;
+      if (load_next) issue_tile(j + 2);
       __builtin_amdgcn_s_setprio(3);
       if constexpr (kPV) {
         const i32x8_t bop = {(int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3],
@@ -245,17 +250,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      // this wave's loads of tile j+1 (issued at the start of its previous softmax half-step)
-      // must have landed before the barrier that ends this half-step
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // this wave's loads of tile j+1 (issued at the start of its previous MFMA half-step) must
+      // have landed before the barrier that ends this half-step; those of tile j+2 may not have
+      if (load_next) __builtin_amdgcn_s_waitcnt(kWaitVm2);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
     };
     const std::true_type yes{};
     const std::false_type no{};
 
-    // VALU half-step: this wave's share of the loads of tile j+2, then the softmax of tile j
-    // (its S^T is in s), leaving P~ in pb.
+    // VALU half-step: the softmax of tile j (its S^T is in s), leaving P~ in pb.
     auto softmax_phase = [&](int j) __attribute__((always_inline)) {
-      if (j + 2 < n_tiles) issue_tile(j + 2);
       // (the whole vector is reinterpreted: __builtin_bit_cast of a single vector element read
       // element 0 whatever the index)
       f32x16_t sf[2];
@@ -307,15 +311,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn8_fwd_kernel(const Params p) 
         }
     };
 
-    // Schedule (as in the bf16 kernel; B_k = k-th workgroup barrier of this query tile).  Every
-    // wave runs  MFMA(j) | barrier | softmax(j) | barrier  for j = 0 .. n-1, then the PV product
-    // of tile n-1, waves 4-7 one barrier behind waves 0-3.  Tile t is loaded into stage t % 4 at
-    // the start of softmax(t-2) -- after B_{2t-3} (group 1) or B_{2t-2} (group 2), both after the
-    // last read of tile t-4 in group 2's MFMA(t-3) -- and waited for at the end of MFMA(t-1),
-    // before the barrier B_{2t} after which group 1 reads it.
+    // Schedule (B_k = k-th workgroup barrier of this query tile, B_0 the one after the prologue).
+    // Every wave runs  MFMA(j) | barrier | softmax(j) | barrier  for j = 0 .. n-1, then the PV
+    // product of tile n-1, waves 4-7 one barrier behind waves 0-3: group 1's MFMA(j) lies between
+    // B_2j and B_2j+1, group 2's between B_2j+1 and B_2j+2.  Tile t is loaded into stage t % 4 at
+    // the start of MFMA(t-2) -- after B_2t-4 (group 1) or B_2t-3 (group 2), so after the last
+    // read of tile t-4, by group 2's PV product in MFMA(t-3), which ends at B_2t-4 -- and waited
+    // for at the end of MFMA(t-1), before the barrier B_2t after which group 1 reads it.  The
+    // prologue loads tiles 0 and 1 and waits for tile 0.
     issue_tile(0);
-    if (n_tiles > 1) issue_tile(1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (n_tiles > 1) {
+      issue_tile(1);
+      __builtin_amdgcn_s_waitcnt(kWaitVm2);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
     barrier();
     if (!first_group) barrier();
     mfma_phase(0, yes, no);
