@@ -175,14 +175,19 @@ __device__ __forceinline__ Params load_params(kernarg_params_t* kp) {
 }
 
 // Attention of one query tile (256 rows of one (batch, head)), run by the whole workgroup.
-// kExact = false: one sweep against the max of the first 64 keys; writes O and returns false, or
-// returns true when some row sum of the tile passed 2^64 (O, written regardless, is then invalid
-// and the caller reruns the tile with kExact = true, which overwrites it).
+// kExact = false: one sweep against the max of the first 64 keys; writes O.  Returns kRedo when
+// some row sum of the tile passed 2^64 (O, written regardless, is then invalid and the caller
+// reruns the tile with kExact = true, which overwrites it).  When next_item >= 0 it also loads
+// the next work item's Q tile into ring stages 2 and 3 once the sweep is done with the ring
+// (the loads overlap this tile's epilogue and vote) and returns kQPrefetched; the caller then
+// passes q_in_lds = true for that item, whose Q operands are read from LDS instead of HBM.
 // kExact = true: one sweep for the row maxima, one softmax sweep against them; writes O.
 // kSplit: work item `item` is key range item % split of query tile item / split; instead of O it
 // writes the unnormalised O, the reference max m and the row sum l of that range to p.ws.
+constexpr int kRedo = 1, kQPrefetched = 2;
 template <bool kExact, bool kSplit>
-__device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) {
+__device__ __forceinline__ int attn_tile(kernarg_params_t* kp, const int item, const int next_item = -1,
+                                         const bool q_in_lds = false) {
   const Params p = load_params(kp);
   const int tile = kSplit ? item / p.split : item;
   const int k0 = kSplit ? (item - tile * p.split) * p.split_tiles * kBN : 0;   // first key of the range
@@ -240,7 +245,10 @@ __device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) 
     // (rows past s_q read as zeros and are never stored)
     bf16x8_t qf[8];
     const int q0 = qt * kBM + wv * 32;
-    {
+    // Q rows staged in LDS by the previous work item (prefetch_q below): row r of the tile sits in
+    // stage 2 (r < 128) or 3, row r % 128, its 16-byte chunk c at position c ^ (r % 16)
+    const unsigned char* q_lds = smem + (2 + (wv >> 2)) * kStageBytes + (32 * (wv & 3) + l32) * 256;
+    if (!q_in_lds) {
       const __amdgpu_buffer_rsrc_t qr =
           make_rsrc(qbase + q0 * stride, (int64_t)(p.s_q - 1 - q0) * stride + kHeadDim * 2);
 #pragma unroll
@@ -443,6 +451,14 @@ __device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) 
       if (n_tiles > 1) issue_tile(1);
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       barrier();
+      if (q_in_lds && kExp && set_ref) {
+        // the Q operands from stages 2 and 3, read before the barrier after which tile 2 is
+        // loaded over them (the first softmax half-step of waves 0-3)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          qf[c] = *reinterpret_cast<const bf16x8_t*>(q_lds + 16 * ((2 * c + h) ^ (l32 & 15)));
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      }
       if (!first_group) barrier();
       mfma_phase(0, yes, no);
       barrier();
@@ -483,6 +499,32 @@ __device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) 
     pair_values(l, la, lb);
     const int row = q0 + l32;
     const Params pe = load_params(kp);   // the output fields, loaded after the sweep
+    // Q of the next work item into ring stages 2 and 3 (the sweep's last barrier passed: no wave
+    // reads the ring any more): wave wv loads its 32 rows, 4 rows of 256 bytes per direct-to-LDS
+    // load, each lane the source chunk that belongs at its LDS position.  Rows past s_q read as
+    // zeros (and are never stored).
+    bool prefetched = false;
+    if constexpr (!kExact) {
+      if (next_item >= 0) {
+        const int ntile = kSplit ? next_item / pe.split : next_item;
+        const int nqt = ntile % pe.q_tiles;
+        const int nbh = ntile / pe.q_tiles;
+        const int nbb = nbh / pe.heads;
+        const int nhh = nbh - nbb * pe.heads;
+        const int nq0 = nqt * kBM;
+        const unsigned char* nq = reinterpret_cast<const unsigned char*>(pe.q) +
+                                  (((int64_t)nbb * pe.s_q + nq0) * pe.heads + nhh) * kHeadDim * 2;
+        const u32x4_t qr = rsrc_words32(nq, (unsigned)(pe.s_q - 1 - nq0) * stride32 + kHeadDim * 2);
+        const unsigned dst = lds_ring + (unsigned)((2 + (wv >> 2)) * kStageBytes + 32 * (wv & 3) * 256);
+        const int sub = lane >> 4, pos = lane & 15;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 32 * wv + 4 * i + sub;   // row of the tile; its row in the stage is r % 128
+          dma_b128(qr, dst + 1024 * i, (unsigned)r * stride32 + 16 * (pos ^ (r & 15)));
+        }
+        prefetched = true;
+      }
+    }
     if constexpr (kSplit) {   // partial result of this key range (the combining kernel divides)
       if (row < pe.s_q) {
         const int64_t r = (int64_t)item * kBM + wv * 32 + l32;
@@ -506,15 +548,39 @@ __device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) 
         // the sum being >= 1 (the reference row max contributes 1 or more)
         if (pe.lse != nullptr && h == 0)
           pe.lse[((int64_t)bb * pe.heads + hh) * pe.s_q + row] = m * kInvSqrtD + __builtin_amdgcn_logf(la + lb) * kLn2;
-        uint16_t* dst = pe.o + (((int64_t)bb * pe.s_q + row) * pe.heads + hh) * kHeadDim + 4 * h;
+      }
+      // O rows through LDS (ring stages 0-1, free after the sweep; the vote's barriers separate these
+      // reads from the next work item's tile loads there), so that each store writes four whole
+      // 256-byte rows instead of 16 bytes of each of 32 rows.  Wave wv stages its 32 rows at
+      // 8 KB * wv; the 16-byte chunk k of row r sits at position k ^ (r % 16).
+      unsigned char* ost = smem + wv * 8192;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
-                         cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
-            *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
-          }
+        for (int g = 0; g < 4; ++g) {
+          u32x2_t x = {cvt_pk_bf16(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                       cvt_pk_bf16(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(ost + l32 * 256 + 16 * ((4 * db + g) ^ (l32 & 15)) + 8 * h) = x;
+        }
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // the wave's own rows: no other wave reads them
+      {
+        const int sub = lane >> 4, pos = lane & 15;
+        const int row0 = q0 + sub;
+        uint16_t* obase_row = pe.o + (((int64_t)bb * pe.s_q + row0) * pe.heads + hh) * kHeadDim;
+        const int64_t row_step = (int64_t)4 * pe.heads * kHeadDim;   // elements between rows 4 apart
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 4 * i + sub;   // row of the wave's 32
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ost + r * 256 + 16 * pos);
+          if (row0 + 4 * i < pe.s_q)
+            *reinterpret_cast<u32x4_t*>(obase_row + i * row_step + 8 * (pos ^ (r & 15))) = x;
+        }
+      }
+      if constexpr (kExact) {
+        // no vote follows the exact path: every wave has read its staged rows before the next
+        // work item loads tiles into these stages
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        barrier();
       }
     }
 
@@ -532,10 +598,10 @@ __device__ __forceinline__ bool attn_tile(kernarg_params_t* kp, const int item) 
       for (int w = 0; w < kWaves; ++w) redo |= redo_flag[w];
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       barrier();   // every wave has read the flags before they are written again
-      if (__builtin_amdgcn_readfirstlane(redo) != 0) return true;
+      if (__builtin_amdgcn_readfirstlane(redo) != 0) return kRedo;
     }
+    return prefetched ? kQPrefetched : 0;
   }
-  return false;
 }
 
 // The value of lane 0 (the same in every lane), as the compiler's uniform value.
@@ -566,10 +632,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
   kernarg_params_t* kp = (kernarg_params_t*)__builtin_amdgcn_kernarg_segment_ptr();
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
+  bool q_in_lds = false;   // this item's Q was loaded into LDS by the previous one
   for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
     const int item = xcd * p.per_xcd + t_local;
     if (item >= p.total) break;
-    if (attn_tile<false, kSplit>(kp, item)) attn_tile_exact<kSplit>(kp, item);
+    const int next = (t_local + p.n_slots < p.per_xcd && item + p.n_slots < p.total) ? item + p.n_slots : -1;
+    const int r = attn_tile<false, kSplit>(kp, item, next, q_in_lds);
+    q_in_lds = (r & kQPrefetched) != 0;
+    if (r & kRedo) {
+      // the exact path reuses the whole ring: the next item loads its Q from HBM again
+      attn_tile_exact<kSplit>(kp, item);
+      q_in_lds = false;
+    }
   }
 }
 
