@@ -19,10 +19,14 @@ bounded sample of query rows of the same workload.
 """
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
+import threading
 import time
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +36,7 @@ METRIC = "attention fwd TFLOP/s and % of MFMA peak at Wan 480p/720p token length
 HEADLINE = "wan14b_720p81f_self"
 PEAK_TFLOPS = {"bf16": 2500.0, "int8_fp8": 5000.0}     # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
+NOMINAL_MHZ = 2400.0           # the clock the dense peaks are quoted at
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "bf16": ["attn_bf16.hip"],
@@ -47,6 +52,75 @@ def source_hash(kind):
     return h.hexdigest()[:16]
 
 
+class ClockSampler:
+    """Samples the GPU's current shader clock in a background thread while a timed region runs; the
+    median of the samples is the clock the chip held there.  It reads the driver's pp_dpm_sclk file
+    (the level marked '*' is the current clock) of the one GPU in sysfs -- no process is started.
+    summary() is None when there is no such single file or no sample landed (regions shorter than
+    one sampling period)."""
+
+    def __init__(self, period_s=0.05):
+        self.period_s = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if len(files) == 1 else None
+
+    def read_mhz(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*mhz", line, flags=re.I)
+                        return int(m.group(1)) if m else None
+        except (OSError, TypeError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self.read_mhz()
+            if v:
+                self.samples.append(v)
+            self._stop.wait(self.period_s)
+
+    def __enter__(self):
+        if self.path is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=5)
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
+                "max_mhz": max(self.samples), "samples": len(self.samples), "source": self.path}
+
+
+def at_clock(frac, clock):
+    """Fraction of the peak scaled to the measured clock (the peak at that clock instead of 2.4 GHz)."""
+    if clock is None or frac is None:
+        return None
+    return frac * NOMINAL_MHZ / clock["median_mhz"]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def measured_traffic(kind, workload):
     """HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken
     on the kernel source as it is now; else None."""
@@ -60,18 +134,22 @@ def measured_traffic(kind, workload):
     return rec.get("bytes_per_launch")
 
 
-def time_calls(fn, steps, warmup, stream):
+def time_calls(fn, steps, warmup, stream, clock=None):
+    """Mean ms per call over `steps` calls after `warmup`; `clock`, if given, is a ClockSampler run
+    across the timed region."""
+    import contextlib
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    end.record(stream)
-    torch.cuda.synchronize()
+    with (clock if clock is not None else contextlib.nullcontext()):
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
 
@@ -92,14 +170,15 @@ def step_stats(fn, steps, stream):
     return statistics.median(times), min(times)
 
 
-def cpu_baseline(w, q, k, v, budget_s=12.0):
-    """The oracle as it stands, on a bounded sample of seeded query rows of the workload: with every BLAS
-    thread, then (a smaller sample) with one."""
-    res = _cpu_baseline_run(w, q, k, v, budget_s)
+def cpu_baseline(w, q, k, v, budget_s=12.0, single_budget_s=None, all_rows=False):
+    """The oracle as it stands, on a bounded sample of seeded query rows of the workload (every row
+    when `all_rows`): with every BLAS thread, then (a smaller budget) with one."""
+    res = _cpu_baseline_run(w, q, k, v, budget_s, all_rows)
+    res["cpu_model"] = cpu_model()
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
-            one = _cpu_baseline_run(w, q, k, v, budget_s / 3)
+            one = _cpu_baseline_run(w, q, k, v, budget_s / 3 if single_budget_s is None else single_budget_s, all_rows)
         res["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1, "sample": one["sample"],
                                 "seconds": one["seconds"]}
     except Exception as e:  # report, do not hide the baseline
@@ -107,7 +186,7 @@ def cpu_baseline(w, q, k, v, budget_s=12.0):
     return res
 
 
-def _cpu_baseline_run(w, q, k, v, budget_s):
+def _cpu_baseline_run(w, q, k, v, budget_s, all_rows=False):
     import numpy as np
     import oracle
     import wan_inputs
@@ -116,8 +195,10 @@ def _cpu_baseline_run(w, q, k, v, budget_s):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = len(os.sched_getaffinity(0))
-    rows_all = wan_inputs.sample_rows(w, 4096).numpy()
-    heads = sorted({(int(r[0]), int(r[1])) for r in rows_all})
+    if all_rows:
+        rows_all = np.array([[bb, hh, i] for bb in range(w.batch) for hh in range(w.heads) for i in range(w.s_q)])
+    else:
+        rows_all = wan_inputs.sample_rows(w, 4096).numpy()
     # host copies of the heads the sample touches, converted exactly from bf16
     def host(t, bh):
         return {p: t[p[0], :, p[1], :].float().cpu().numpy() for p in bh}
@@ -142,14 +223,17 @@ def _cpu_baseline_run(w, q, k, v, budget_s):
             break
         n = min(len(rows_all) - done_rows, max(8, int(n * 2)))
     flops = 4 * done_rows * w.s_kv * w.head_dim
+    total_rows = w.batch * w.heads * w.s_q
+    what = "every query row" if all_rows and done_rows == total_rows else f"{done_rows} seeded query rows"
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done_rows} seeded query rows of {w.name} (fp64 two-pass oracle, "
+            "sample": f"{what} of {w.name} (fp64 two-pass oracle, "
                       f"{done_rows / elapsed:.2f} rows/s; full workload extrapolates to "
-                      f"{w.batch * w.heads * w.s_q / (done_rows / elapsed) / 3600:.1f} h)",
-            "seconds": round(elapsed, 2)}
+                      f"{total_rows / (done_rows / elapsed):.1f} s)",
+            "rows": int(done_rows), "seconds": round(elapsed, 2),
+            "full_workload_s": round(total_rows / (done_rows / elapsed), 1)}
 
 
-def run_workload(name, steps, warmup):
+def run_workload(name, steps, warmup, cpu_budget_s=0.0):
     import torch
     import video_diffusion_transformer_wan_amd as wan
     import wan_inputs
@@ -159,11 +243,14 @@ def run_workload(name, steps, warmup):
     stream = torch.cuda.current_stream()
     fn = lambda: wan.wan_attn_fwd(q, k, v, out, w.batch, w.heads, w.s_q, w.s_kv, w.head_dim, w.path,
                                   stream)
-    ms = time_calls(fn, steps, warmup, stream)
+    clock = ClockSampler()
+    ms = time_calls(fn, steps, warmup, stream, clock)
     med, mn = step_stats(fn, steps, stream)
     res = {"workload": name, "path": w.path, "ms": ms, "tflops": w.flops / (ms * 1e-3) / 1e12,
            "ms_median": med, "ms_min": mn}
     res["frac_of_peak"] = res["tflops"] / PEAK_TFLOPS[w.path]
+    res["clock"] = clock.summary()
+    res["frac_of_peak_at_measured_clock"] = at_clock(res["frac_of_peak"], res["clock"])
     kernel_ms = ms
     if w.path == "int8_fp8":
         # the attention kernel alone, from pre-quantised operands
@@ -173,7 +260,18 @@ def run_workload(name, steps, warmup):
         res["kernel_ms"] = kernel_ms
         res["kernel_tflops"] = w.flops / (kernel_ms * 1e-3) / 1e12
         res["kernel_frac_of_peak"] = res["kernel_tflops"] / PEAK_TFLOPS[w.path]
+        res["kernel_frac_of_peak_at_measured_clock"] = at_clock(res["kernel_frac_of_peak"], res["clock"])
+        # the softmax's VALU floor (measured per-instruction costs beside a busy matrix core, per
+        # 64-key tile and wave: 32 v_fma_f32 x 7.5 + 32 v_exp_f32 x 13.2 + 16 v_cvt_pk_fp8_f32 x 12.6 +
+        # 16 v_max3_f32 x 8.6 + 12 others x 8 cycles), at the measured clock
+        if res["clock"] is not None:
+            cyc = 32 * 7.5 + 32 * 13.2 + 16 * 12.6 + 16 * 8.6 + 12 * 8
+            wave_tiles = w.batch * w.heads * w.s_q * w.s_kv / (32 * 64)
+            res["valu_floor_ms"] = wave_tiles / 1024 * cyc / (res["clock"]["median_mhz"] * 1e6) * 1e3
         del z
+    if cpu_budget_s > 0:
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, cpu_budget_s, cpu_budget_s / 2,
+                                           all_rows=w.batch * w.heads * w.s_q <= 4096)
     return w, (q, k, v), res, kernel_ms
 
 
@@ -271,7 +369,25 @@ def run_vsa(name, steps, warmup):
             "sparsity": 1.0 - w.keep / -(-s // 64), "ms": ms, "tflops": tf, "fine_ms": fine_ms,
             "fine_tflops": ftf, "fine_frac_of_peak": ftf / PEAK_TFLOPS["bf16"], "coarse_ms": coarse_ms,
             "dense_ms": dense_ms, "speedup_vs_dense": dense_ms / ms, "fine_speedup_vs_dense": dense_ms / fine_ms,
-            "flops": flops, "gathered_bytes": gathered, "gather_tbps": gathered / (fine_ms * 1e-3) / 1e12}
+            "flops": flops, "gathered_bytes": gathered, "gather_tbps": gathered / (fine_ms * 1e-3) / 1e12,
+            "fine_hbm": vsa_fine_hbm(name, fine_ms)}
+
+
+def vsa_fine_hbm(name, fine_ms):
+    """The fine stage against the HBM roofline it is bound by: the bytes it fetches from beyond L2 per
+    launch (rocprofv3 FETCH_SIZE, scaled by the copy calibration; profiles/traffic.json, used only while
+    vsa.hip is the source the counters were taken on) over its time, against 8 TB/s."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(f"vsa_fine:{name}")
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256(open(os.path.join(HERE, "video_diffusion_transformer_wan_amd", "csrc", "vsa.hip"), "rb").read())
+    if not rec or rec.get("source_hash") != h.hexdigest()[:16]:
+        return None
+    gbs = rec["fetch_bytes"] / (fine_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": rec["fetch_bytes"]}
 
 
 def main():
@@ -320,6 +436,7 @@ def main():
     wan.lib()
 
     w, qkv, head, kernel_ms = run_workload(args.workload, args.steps, args.warmup)
+    clock = head.get("clock")
     flops = w.flops
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     # secondary ceiling: one exponential per score, at the v_exp_f32 rate measured on gfx950 (28.4 lane
@@ -329,6 +446,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[w.path],
             "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[w.path], 4),
             "traffic": measured_traffic(w.path, w.name),
+            "clock": clock, "frac_at_measured_clock": at_clock(achieved / PEAK_TFLOPS[w.path], clock),
             "kernel": "attn_fwd_bf16_kernel" if w.path == "bf16" else "attn8_fwd_kernel",
             "flops_per_launch": flops,
             "exp_ceiling": {"exps_per_launch": exps, "ms_at_exp_rate": round(exp_ms, 3),
@@ -347,7 +465,8 @@ def main():
             small = wan_inputs.WORKLOADS[name].flops < 1e13
             try:
                 _, _, res, _ = run_workload(name, args.steps * (10 if small else 1),
-                                            args.warmup * (5 if small else 1))
+                                            args.warmup * (5 if small else 1),
+                                            cpu_budget_s=0.0 if args.no_cpu else 3.0)
             except Exception as e:  # report, do not hide the headline
                 res = {"workload": name, "error": str(e)}
             configs[name] = res
