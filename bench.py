@@ -2,6 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra] [--no-cpu]
 python bench.py --backward-only NAME | --linear-only NAME | --vsa-only NAME   (one path alone, for profiling)
+python bench.py --mfma-ceiling   (sustained matrix-core rate of each MFMA instruction, the practical ceiling)
 
 One step = one call of the C ABI's wan_attn_fwd on the workload's full shape, inputs already in
 HBM.  Prints ONE JSON line: the headline is the bf16 self-attention of the Wan-14B-shaped 720p,
@@ -233,6 +234,63 @@ def _cpu_baseline_run(w, q, k, v, budget_s, all_rows=False):
             "full_workload_s": round(total_rows / (done_rows / elapsed), 1)}
 
 
+CEILING_KINDS = [  # (kind, instruction, operations per wave-iteration, dense peak in TFLOP/s at 2.4 GHz)
+    (0, "v_mfma_f32_32x32x16_bf16", 8 * 32768, 2500.0),
+    (1, "v_mfma_f32_16x16x32_bf16", 16 * 16384, 2500.0),
+    (2, "v_mfma_f32_32x32x64_f8f6f4 (e4m3)", 8 * 131072, 5000.0),
+    (3, "v_mfma_i32_32x32x32_i8", 8 * 65536, 5000.0),
+    (4, "v_mfma_f32_16x16x128_f8f6f4 (e4m3)", 16 * 65536, 5000.0),
+    (5, "v_mfma_i32_16x16x64_i8", 16 * 32768, 5000.0),
+]
+
+
+def run_mfma_ceiling(target_ms=150.0, launches=5):
+    """Sustained matrix-core rate: one wave per SIMD on every compute unit streaming independent MFMAs
+    with operands from registers (random bf16 / e4m3 / int8 bit patterns that change between
+    instructions), each launch about target_ms long so that the chip settles at the clock its power
+    limit gives that load; HIP events on the launch stream, the shader clock sampled meanwhile."""
+    import ctypes
+    import torch
+    from video_diffusion_transformer_wan_amd import build as wan_build
+    if not os.path.exists(wan_build.CEILING_LIB):
+        raise RuntimeError(f"{wan_build.CEILING_LIB} is not built (python -m video_diffusion_transformer_wan_amd.build)")
+    lib = ctypes.CDLL(wan_build.CEILING_LIB)
+    lib.wan_mfma_ceiling_run.restype = ctypes.c_int
+    lib.wan_mfma_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_void_p]
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device="cpu").manual_seed(7)
+    out = torch.empty(n_wg * 4, dtype=torch.float32, device="cuda")
+    res = {"workgroups": n_wg, "waves_per_simd": 1, "launch_ms_target": target_ms, "kinds": []}
+    for kind, name, ops, peak in CEILING_KINDS:
+        if kind in (0, 1):      # N(0,1) bf16 values
+            src = torch.randn(64 * 8 * 16, generator=g).to(torch.bfloat16).view(torch.uint8)
+        elif kind in (2, 4):    # N(0,1) e4m3 values (finite codes)
+            src = torch.randn(64 * 8 * 32, generator=g).to(torch.float8_e4m3fn).view(torch.uint8)
+        else:                   # uniform int8
+            src = torch.randint(-127, 128, (64 * 8 * 32,), generator=g, dtype=torch.int8).view(torch.uint8)
+        src = src.to("cuda")
+
+        def launch(iters):
+            rc = lib.wan_mfma_ceiling_run(kind, src.data_ptr(), out.data_ptr(), n_wg, iters, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"wan_mfma_ceiling_run returned {rc}")
+        probe_iters = 20000
+        ms = time_calls(lambda: launch(probe_iters), 1, 1, stream)
+        iters = int(min(2 ** 30, max(probe_iters, probe_iters * target_ms / ms)))
+        clock = ClockSampler()
+        ms = time_calls(lambda: launch(iters), launches, 1, stream, clock=clock)
+        flops = n_wg * 4 * iters * ops
+        tf = flops / (ms * 1e-3) / 1e12
+        clk = clock.summary()
+        res["kinds"].append({"instruction": name, "iters": iters, "ms": round(ms, 3), "tflops": round(tf, 1),
+                             "frac_of_peak": round(tf / peak, 4), "clock": clk,
+                             "frac_at_measured_clock": at_clock(tf / peak, clk)})
+        print(json.dumps(res["kinds"][-1]), flush=True)
+    return res
+
+
 def run_workload(name, steps, warmup, cpu_budget_s=0.0):
     import torch
     import video_diffusion_transformer_wan_amd as wan
@@ -404,6 +462,8 @@ def main():
                     help="only time the FP8 linear at this projection shape (for profiling)")
     ap.add_argument("--vsa-only", default=None, metavar="WORKLOAD",
                     help="only time the block-sparse attention at this shape (for profiling)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the sustained matrix-core rate of each MFMA instruction the kernels use")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -421,6 +481,9 @@ def main():
             y.copy_(x)
         torch.cuda.synchronize()
         print(json.dumps({"copy_mib": args.copy_mib, "dispatches": max(1, args.steps)}), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps(run_mfma_ceiling()), flush=True)
         return
     if args.backward_only or args.linear_only or args.vsa_only:
         res = (run_backward(args.backward_only, args.steps, args.warmup) if args.backward_only

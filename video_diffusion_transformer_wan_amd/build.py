@@ -1,4 +1,6 @@
-"""Build libwan_attn.so in-tree with hipcc for gfx950 (python -m video_diffusion_transformer_wan_amd.build)."""
+"""Build libwan_attn.so in-tree with hipcc for gfx950 (python -m video_diffusion_transformer_wan_amd.build),
+and beside it libwan_mfma_ceiling.so, the sustained matrix-core rate measurement that the benchmark runs
+(csrc/ceiling/, not part of the attention library)."""
 
 import os
 import shutil
@@ -10,6 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libwan_attn.so")
+CEILING_LIB = os.path.join(PKG, "libwan_mfma_ceiling.so")
 
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.  -fno-honor-nans: the kernels
@@ -32,17 +35,23 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every HIP source of the package into libwan_attn.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources()]
+def _compile(out, srcs, extra_flags, verbose):
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose=False, extra_flags=()):
+    """Compile every HIP source of the package into libwan_attn.so and the measurement kernel into
+    libwan_mfma_ceiling.so (always recompiles both)."""
+    _compile(LIB, sources(), extra_flags, verbose)
+    _compile(CEILING_LIB, [os.path.join(CSRC, "ceiling", "mfma_ceiling.hip")], (), verbose)
     return LIB
 
 
