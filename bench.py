@@ -57,10 +57,10 @@ class ClockSampler:
     """Samples the GPU's current shader clock in a background thread while a timed region runs; the
     median of the samples is the clock the chip held there.  It reads the driver's pp_dpm_sclk file
     (the level marked '*' is the current clock) of the one GPU in sysfs -- no process is started.
-    summary() is None when there is no such single file or no sample landed (regions shorter than
-    one sampling period)."""
+    summary() is None when there is no such single file or fewer than 3 samples landed after the first
+    (regions shorter than about 40 ms)."""
 
-    def __init__(self, period_s=0.05):
+    def __init__(self, period_s=0.01):
         self.period_s = period_s
         self.samples = []
         self._stop = threading.Event()
@@ -98,10 +98,13 @@ class ClockSampler:
             self._thread.join(timeout=5)
 
     def summary(self):
-        if not self.samples:
+        # the first sample can predate the first launch (the idle clock): dropped; a region with fewer
+        # than 3 samples after it reports no clock
+        kept = self.samples[1:]
+        if len(kept) < 3:
             return None
-        return {"median_mhz": statistics.median(self.samples), "min_mhz": min(self.samples),
-                "max_mhz": max(self.samples), "samples": len(self.samples), "source": self.path}
+        return {"median_mhz": statistics.median(kept), "min_mhz": min(kept),
+                "max_mhz": max(kept), "samples": len(kept), "source": self.path}
 
 
 def at_clock(frac, clock):
