@@ -166,7 +166,8 @@ def test_frame480_all_rows():
     out = wan.attention(q, k, v)
     torch.cuda.synchronize()
     ref = oracle.attention(to_np(q), to_np(k), to_np(v))
-    rel, mx, _ = metrics(to_np(out), ref)
+    rel, mx, cos = metrics(to_np(out), ref)
+    print(f"workload frame480_self (every row): rel-L2 {rel:.3e} max-abs {mx:.3e} cos {cos:.6f}", flush=True)
     assert rel <= BF16_REL_L2 and mx <= BF16_MAX_ABS
 
 
