@@ -360,3 +360,24 @@ def test_noalloc_backward_size_limit():
     bad[5] = None
     assert lib.wan_attn_bwd_noalloc(*bad, 1, 1, 64, 64, 128, None) == wan.WAN_ATTN_EINVAL
     assert lib.wan_attn_bwd_noalloc(*ptrs, 1, 1, 64, 64, 64, None) == wan.WAN_ATTN_EUNSUPPORTED
+
+
+def test_mfma_ceiling_library_rejects_bad_arguments():
+    # the measurement library beside the attention library: it loads without a GPU and refuses
+    # arguments it cannot launch with (null buffers, no workgroups, no iterations, unknown kind)
+    # before touching the device
+    from video_diffusion_transformer_wan_amd import build as wan_build
+    ensure_built()
+    if not os.path.exists(wan_build.CEILING_LIB):
+        wan_build.build()
+    lib = ctypes.CDLL(wan_build.CEILING_LIB)
+    f = lib.wan_mfma_ceiling_run
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    fake = 4096   # never dereferenced: every call below is refused first
+    assert f(0, None, fake, 256, 10, None) == 1
+    assert f(0, fake, None, 256, 10, None) == 1
+    assert f(0, fake, fake, 0, 10, None) == 1
+    assert f(0, fake, fake, 256, 0, None) == 1
+    assert f(6, fake, fake, 256, 10, None) == 1
+    assert f(-1, fake, fake, 256, 10, None) == 1
