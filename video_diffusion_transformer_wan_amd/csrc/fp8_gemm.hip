@@ -22,8 +22,9 @@
 //    row, so every row is one whole line), one to two steps ahead, rows past M or N reading as
 //    zeros.  Chunk c of tile row r sits at chunk c ^ swz(r), which keeps the operand reads free of
 //    bank conflicts (the LDS serves the 16 lanes of a half-wave whose bits 2, 3 and 4 have the same
-//    parity together; measured, not documented).  Workgroups are numbered so that the 32 CUs of one
-//    XCD share 4 token tiles and 8 feature tiles in their L2.
+//    parity together; measured, not documented).  Persistent (one workgroup per CU) and XCD-aware:
+//    the 32 CUs of one XCD share 4 token tiles and 8 feature tiles in their L2, and each workgroup
+//    loads its next tile's first operand tiles behind its stores.
 
 #include <type_traits>
 
@@ -153,7 +154,7 @@ struct GemmParams {
   uint16_t* y;            // [m][n] bf16
   int64_t m, n;
   int k;
-  int tiles_m, tiles_n, total, per_xcd;
+  int tiles_m, tiles_n, total, per_xcd, n_slots;
 };
 
 // 16-byte chunk c of tile row r sits at chunk c ^ swz(r) of the row's 128 bytes
@@ -178,25 +179,26 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 
 __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kSlots * kTileBytes];
-  // XCD-aware numbering: workgroup b runs on XCD b % 8 and takes work item (b % 8) * per_xcd +
-  // b / 8; items run token-tile-major in groups of kGroupM token tiles, so the workgroups of one
-  // XCD share a few X and W tiles in L2.
-  const int b = blockIdx.x;
-  const int t = (b & 7) * p.per_xcd + (b >> 3);
-  if (t >= p.total) return;
-  const int group = t / (kGroupM * p.tiles_n);
-  const int first_m = group * kGroupM;
-  const int gm = min(kGroupM, p.tiles_m - first_m);
-  const int in_group = t - group * kGroupM * p.tiles_n;
-  const int mt = first_m + in_group % gm;
-  const int nt = in_group / gm;
+  // Persistent and XCD-aware: workgroup b runs on XCD b % 8 and takes work items (b % 8) * per_xcd +
+  // b / 8 + i * n_slots of that XCD's contiguous range; items run token-tile-major in groups of
+  // kGroupM token tiles, so the workgroups of one XCD share a few X and W tiles in L2.  The next
+  // item's first five operand tiles are loaded at the end of each item, after its stores.
+  const int xcd = blockIdx.x & 7;
+  const int slot_id = blockIdx.x >> 3;
+  auto item_tiles = [&](int t, int& mt, int& nt) __attribute__((always_inline)) {
+    const int group = t / (kGroupM * p.tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, p.tiles_m - first_m);
+    const int in_group = t - group * kGroupM * p.tiles_n;
+    mt = first_m + in_group % gm;
+    nt = in_group / gm;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 1, wn = wv & 1;
   const int l16 = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)mt * kTM, n0 = (int64_t)nt * kTN;
   const int K = p.k;
   const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
 
@@ -207,8 +209,14 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
   // one whole 128-byte line.  One descriptor per operand over its valid rows (rows past m or n read
   // as zeros); the K position is the scalar offset.  When k is an odd multiple of 64, the lanes of
   // the last step's upper 64 bytes point past the descriptor and read zeros.
-  const u32x4_t wr = rsrc_words(p.w + n0 * K, min((int64_t)kTN, p.n - n0) * K);
-  const u32x4_t xr = rsrc_words(p.x + m0 * K, min((int64_t)kTM, p.m - m0) * K);
+  auto w_rsrc = [&](int nt) __attribute__((always_inline)) {
+    const int64_t n0 = (int64_t)nt * kTN;
+    return rsrc_words(p.w + n0 * K, min((int64_t)kTN, p.n - n0) * K);
+  };
+  auto x_rsrc = [&](int mt) __attribute__((always_inline)) {
+    const int64_t m0 = (int64_t)mt * kTM;
+    return rsrc_words(p.x + m0 * K, min((int64_t)kTM, p.m - m0) * K);
+  };
   unsigned src_off[4];
   bool upper[4];
 #pragma unroll
@@ -221,7 +229,7 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
   const int n_steps = (K + kTK - 1) / kTK;
   const int n_tiles = 2 * n_steps;
   const bool half_last = (K % kTK) != 0;
-  auto issue_block = [&](int u, int it) __attribute__((always_inline)) {
+  auto issue_block_of = [&](const u32x4_t& wr, const u32x4_t& xr, int u, int it) __attribute__((always_inline)) {
     const int s = u >> 1;
     const u32x4_t rs = (u & 1) ? xr : wr;
     const unsigned koff = (unsigned)(s * kTK);
@@ -229,9 +237,9 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
     const bool cut = half_last && s == n_steps - 1;
     dma_b128(rs, st + 1024 * (4 * wv + it), (cut && upper[it]) ? 0x80000000u : src_off[it], koff);
   };
-  auto issue = [&](int u) __attribute__((always_inline)) {
+  auto issue_of = [&](const u32x4_t& wr, const u32x4_t& xr, int u) __attribute__((always_inline)) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) issue_block(u, it);
+    for (int it = 0; it < 4; ++it) issue_block_of(wr, xr, u, it);
   };
 
   // Operands of v_mfma_f32_16x16x128_f8f6f4: a lane feeds row l16 of a 16-row block and the 32
@@ -253,6 +261,16 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
   auto read_b = [&](int s, int ti) __attribute__((always_inline)) { return read_op(slot(2 * s + 1), 64 * wm + 16 * ti); };
 
   typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+  bool prefetched = false;   // this item's first operand tiles were loaded by the previous item
+  for (int t_local = slot_id; t_local < p.per_xcd; t_local += p.n_slots) {
+  const int t = xcd * p.per_xcd + t_local;
+  if (t >= p.total) break;
+  int mt, nt;
+  item_tiles(t, mt, nt);
+  const int64_t m0 = (int64_t)mt * kTM, n0 = (int64_t)nt * kTN;
+  const u32x4_t wr = w_rsrc(nt), xr = x_rsrc(mt);
+  auto issue_block = [&](int u, int it) __attribute__((always_inline)) { issue_block_of(wr, xr, u, it); };
+  auto issue = [&](int u) __attribute__((always_inline)) { issue_of(wr, xr, u); };
   f32x4_t acc[8][4];
 #pragma unroll
   for (int fi = 0; fi < 8; ++fi)
@@ -266,8 +284,10 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
   // slower).  Before M_s every wave has waited for its own loads of tiles 2s+2, 2s+3 (only those of
   // 2s+4, all issued during step s, may still be in flight) and for its own operand reads of step s;
   // after it, it reads step s+1's B operands and first A.
-  for (int u = 0; u < min(kSlots, n_tiles); ++u) issue(u);
-  // tiles 0 and 1 landed; n_tiles is even, so 0, 2 or 3 tiles may still be in flight
+  if (!prefetched)
+    for (int u = 0; u < min(kSlots, n_tiles); ++u) issue(u);
+  // tiles 0 and 1 landed; n_tiles is even, so 0, 2 or 3 tiles may still be in flight (the previous
+  // item's stores, issued before these loads, only make the count larger)
   if (n_tiles >= kSlots) __builtin_amdgcn_s_waitcnt(0x0F70 | (3 * kLoadsPerSlot));
   else if (n_tiles == 4) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerSlot));
   else __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -330,6 +350,18 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
       *reinterpret_cast<u32x2_t*>(yrow + n) = v;
     }
   }
+  // The next item's first operand tiles, after this item's stores (so that the next item's counted
+  // waits for them stay exact).  Every wave finished its reads of this item's operands before the
+  // barrier of the last step (what it read after that was a stale slot, unused).
+  prefetched = false;
+  if (t_local + p.n_slots < p.per_xcd && t + p.n_slots < p.total) {
+    int nmt, nnt;
+    item_tiles(t + p.n_slots, nmt, nnt);
+    const u32x4_t nwr = w_rsrc(nnt), nxr = x_rsrc(nmt);
+    for (int u = 0; u < min(kSlots, n_tiles); ++u) issue_of(nwr, nxr, u);
+    prefetched = true;
+  }
+  }
 }
 
 }  // namespace
@@ -370,7 +402,12 @@ hipError_t launch_fp8_gemm(const void* x_codes, const float* x_scales, const voi
   p.tiles_n = (int)ceil_div(n, kTN);
   p.total = p.tiles_m * p.tiles_n;
   p.per_xcd = (int)ceil_div(p.total, 8);
-  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)(8 * p.per_xcd)), dim3(kGThreads), 0, stream, p);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 8)
+    cus = 256;
+  p.n_slots = p.per_xcd < cus / 8 ? p.per_xcd : cus / 8;   // one workgroup per CU
+  hipLaunchKernelGGL(fp8_gemm_kernel, dim3((unsigned)(8 * p.n_slots)), dim3(kGThreads), 0, stream, p);
   return hipGetLastError();
 }
 
