@@ -633,6 +633,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(const Params
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   bool q_in_lds = false;   // this item's Q was loaded into LDS by the previous one
+  // Short key sequences (at most 16 tiles: the text cross-attention): work items are short and all
+  // of equal length, so every CU would load Q and store O at the same moments.  The odd slots start
+  // about a quarter of a work item late (0.5 us per key tile on the 100 MHz real-time counter; the
+  // wait is capped), so that the two halves of the CUs reach their item boundaries at different
+  // times.
+  if ((slot & 1) && p.split == 1 && p.s_kv <= 16 * kBN) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t d = 50ull * (uint64_t)((p.s_kv + kBN - 1) / kBN);
+    for (int it = 0; it < 4096 && __builtin_amdgcn_s_memrealtime() - t0 < d; ++it) __builtin_amdgcn_s_sleep(4);
+  }
   for (int t_local = slot; t_local < p.per_xcd; t_local += p.n_slots) {
     const int item = xcd * p.per_xcd + t_local;
     if (item >= p.total) break;
