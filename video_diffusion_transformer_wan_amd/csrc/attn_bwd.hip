@@ -10,11 +10,12 @@
 //  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) and D = rowsum(dO * O) per query row, f32, per
 //    64-row query tile [b*H][s_q_pad / 64][lse2 x 64 | D x 64]; padding rows get lse2 = 1e30 (so
 //    P = 0) and D = 0.
-//  * attn_bwd_dq_kernel -- one workgroup = 4 waves = 128 query rows of one (batch, head); each lane
+//  * attn_bwd_dq_kernel -- one workgroup = 8 waves = 256 query rows of one (batch, head); each lane
 //    owns one query row (transposed products, as in the forward):
 //        S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
 //        dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
-//    looping over 64-key tiles of K and V streamed through a 2-stage LDS ring.
+//    looping over 64-key tiles of K and V streamed through a 4-stage LDS ring, waves 0-3 and 4-7
+//    in ping-pong (one group's S^T / dP^T products against the other's VALU work and dQ product).
 //  * attn_bwd_dkdv_kernel -- one workgroup = 8 waves = 128 keys; each lane owns one key, and two
 //    waves share each group of 32 keys (and a SIMD):
 //        P wave:  S = Q K^T, P,             dV^T += dO^T P
@@ -44,9 +45,7 @@ typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;             // query rows (dQ kernel) or keys (dK/dV kernel) per workgroup
+constexpr int kRows = 128;                     // keys per dK/dV workgroup
 constexpr int kTile = 64;                      // rows per streamed LDS tile
 constexpr int kTileBytes = kTile * kHeadDim * 2;   // 16 KB
 constexpr int kStatBytes = 1024;               // lse2 and D of a query tile (512 bytes, loaded twice)
@@ -69,7 +68,7 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   int heads, s_q, s_kv, s_q_pad;
-  int q_blocks;       // 128-row query blocks per (b, h)  (dQ kernel)
+  int q_blocks;       // 256-row query blocks per (b, h)  (dQ kernel)
   int k_blocks;       // 128-key blocks per (b, h)        (dK/dV kernel)
 };
 
@@ -218,19 +217,40 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, i
 }
 
 // ---------------------------------------------------------------------------------------------
-// Stage 2a: dQ.
-__global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * kTileBytes];   // [stage][K | V]
+// Stage 2a: dQ.  One workgroup = 8 waves = 256 query rows of one (batch, head); each lane owns one
+// query row, and the products run transposed, as in the forward:
+//     S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
+//     dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
+// Each wave's work on a 64-key tile is split into two half-steps between workgroup barriers:
+// (1) S^T and dP^T of tile j; (2) the loads of tile j+2, dS of tile j and the dQ product.  Waves
+// 0-3 and 4-7 share the four SIMDs and run one barrier apart, so each SIMD's matrix core takes one
+// wave's S^T / dP^T products while the other wave runs its VALU work and then its dQ product.
+// The dQ^T accumulators are MFMA builtins in VGPRs (256 per lane, no AGPRs): pinned to AGPRs by
+// inline asm they would make the compiler split the register file 128 / 128, and the S^T, dP^T
+// and operand registers would not fit in 128 VGPRs.  64-key tiles of K and V stream through a
+// 4-stage LDS ring: tile t is loaded at the start of half-step (2) of tile t-2 -- after every read
+// of tile t-4, the last being the second group's dQ product of tile t-4, two barriers earlier --
+// and waited for at the end of half-step (1) of tile t-1, before the barrier after which the first
+// group reads it.
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRows = 32 * kDqWaves;      // 256 query rows per workgroup
+constexpr int kDqStage = 2 * kTileBytes;    // [K | V], 32 KB
+constexpr int kDqRing = 4;
+
+__global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDqRing * kDqStage];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool first_group = wv < kDqWaves / 2;
   const int l32 = lane & 31;
   const int h = lane >> 5;
   const int bh = blockIdx.x / p.q_blocks;
   const int qblk = blockIdx.x - bh * p.q_blocks;
   const int bb = bh / p.heads, hh = bh - bb * p.heads;
   const int64_t stride = (int64_t)p.heads * kHeadDim * 2;
-  const int q0 = qblk * kRows + 32 * wv;
+  const int q0 = qblk * kDqRows + 32 * wv;
   const int qrow = q0 + l32;
   const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
 
@@ -248,6 +268,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
   }
   const float lse2 = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow)] : kPadLse2;
   const float dsum = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow) + 64] : 0.0f;
+  // waited for here, before any direct-to-LDS load is issued: the compiler does not see those, and
+  // would otherwise place its wait for these registers inside the tile loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int64_t kvoff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2;
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(p.k) + kvoff;
@@ -256,9 +279,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
   const int n_kt = (p.s_kv + kTile - 1) / kTile;
   auto issue = [&](int j) __attribute__((always_inline)) {
     const int64_t off = (int64_t)j * kTile * stride;
-    const unsigned st = lds + (unsigned)((j & 1) * 2 * kTileBytes);
-    load_tile<kWaves>(kbase + off, kvbytes - off, stride, st, wv, lane);
-    load_tile<kWaves>(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
+    const unsigned st = lds + (unsigned)((j % kDqRing) * kDqStage);
+    load_tile<kDqWaves>(kbase + off, kvbytes - off, stride, st, wv, lane);
+    load_tile<kDqWaves>(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
   };
 
   f32x16_t acc[4];
@@ -268,23 +291,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
   issue(0);
-  barrier_all();
+  if (n_kt > 1) issue(1);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  barrier();
+  if (!first_group) barrier();
   for (int j = 0; j < n_kt; ++j) {
-    if (j + 1 < n_kt) issue(j + 1);   // stage (j+1) & 1: free since the barrier that ended tile j-1
-    const unsigned char* ks = smem + (j & 1) * 2 * kTileBytes;
+    const unsigned char* ks = smem + (j % kDqRing) * kDqStage;
     const unsigned char* vs = ks + kTileBytes;
+    // (1) S^T and dP^T of tile j
+    __builtin_amdgcn_s_setprio(3);
     f32x16_t s[2], dp[2];
+    const f32x16_t zero = {};
+    // one step = the 4 MFMAs of 16 channels; its LDS operands are read one step ahead
+    bf16x8_t ring[2][4];
+    auto read_step = [&](int c, bf16x8_t (&f)[4]) __attribute__((always_inline)) {
+      f[0] = read_rows(ks, 0, c, l32, h);
+      f[1] = read_rows(ks, 1, c, l32, h);
+      f[2] = read_rows(vs, 0, c, l32, h);
+      f[3] = read_rows(vs, 1, c, l32, h);
+    };
+    read_step(0, ring[0]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = dp[kb][r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(ks, kb, c, l32, h), qf[c], s[kb], 0, 0, 0);
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(vs, kb, c, l32, h), gf[c], dp[kb], 0, 0, 0);
-      }
+    for (int c = 0; c < 8; ++c) {
+      const int cur = c & 1;
+      if (c + 1 < 8) read_step(c + 1, ring[cur ^ 1]);
+      s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][0], qf[c], c == 0 ? zero : s[0], 0, 0, 0);
+      s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][1], qf[c], c == 0 ? zero : s[1], 0, 0, 0);
+      dp[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][2], gf[c], c == 0 ? zero : dp[0], 0, 0, 0);
+      dp[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[cur][3], gf[c], c == 0 ? zero : dp[1], 0, 0, 0);
+      if (c + 1 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // this wave's loads of tile j+1 (issued in half-step (2) of tile j-1) have landed
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    barrier();
+    // (2) the loads of tile j+2; dS of tile j; dQ^T += K^T dS^T over the tile's 4 steps of 16 keys
+    if (j + 2 < n_kt) issue(j + 2);
     // register r of key block kb holds key 64 j + 32 kb + 16 (r / 8) + 8 h + r % 8 of this lane's row
     unsigned ds[2][8];
     const int kv0 = j * kTile;
@@ -302,21 +346,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_bwd_dq_kernel(const BwdParam
         const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sb, kScaleLog2, -lse2));
         ds[kb][r >> 1] = cvt_pk_bf16(pa * (dp[kb][r] - dsum), pb * (dp[kb][r + 1] - dsum));
       }
-    // dQ^T += K^T dS^T over the tile's 4 steps of 16 keys
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int kb = t >> 1, u = t & 1;
       const u32x4_t x = {ds[kb][4 * u], ds[kb][4 * u + 1], ds[kb][4 * u + 2], ds[kb][4 * u + 3]};
       const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, x);
-      bf16x8_t a[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) a[db] = read_cols(ks, t, db, lane);
-      mfma4_acc(acc, a, bop);
+      for (int db = 0; db < 4; ++db)
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(ks, t, db, lane), bop, acc[db], 0, 0, 0);
     }
-    barrier_all();   // tile j+1 has landed; every wave is done with stage j & 1
+    barrier();
   }
+  if (first_group) barrier();
 
-  settle_mfma(acc);
   // dQ = dQ^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of row qrow
   if (qrow < p.s_q) {
     uint16_t* dst = p.dq + (((int64_t)bb * p.s_q + qrow) * p.heads + hh) * kHeadDim + 4 * h;
@@ -637,13 +679,13 @@ hipError_t launch_attn_bwd(const void* q, const void* k, const void* v, const vo
   p.dq = static_cast<uint16_t*>(dq);
   p.dk = static_cast<uint16_t*>(dk);
   p.dv = static_cast<uint16_t*>(dv);
-  p.q_blocks = (int)ceil_div(sh.s_q, kRows);
+  p.q_blocks = (int)ceil_div(sh.s_q, kDqRows);
   p.k_blocks = (int)ceil_div(sh.s_kv, kRows);
   const int64_t rows = bh * p.s_q_pad;
   hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3((unsigned)ceil_div(rows, 32)), dim3(256), 0, stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(bh * p.q_blocks)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(attn_bwd_dq_kernel, dim3((unsigned)(bh * p.q_blocks)), dim3(kDqThreads), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_bwd_dkdv_kernel, dim3((unsigned)(bh * p.k_blocks)), dim3(kKvThreads), 0, stream, p);
