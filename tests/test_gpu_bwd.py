@@ -81,7 +81,7 @@ def test_forward_lse(b, H, s_q, s_kv):
 
 
 @pytest.mark.parametrize("s_q,s_kv", [(1, 1), (1, 200), (64, 64), (65, 63), (127, 129), (129, 127), (300, 1),
-                                      (200, 300), (256, 256)])
+                                      (200, 300), (256, 256), (257, 320), (511, 257)])
 def test_backward_ragged(s_q, s_kv):
     _full_case(1, 2, s_q, s_kv, seed=3000 + 7 * s_q + s_kv)
 
