@@ -79,7 +79,10 @@ def _quantize_both(x, w):
     return xc, xs, wc, ws
 
 
-@pytest.mark.parametrize("m,k", [(1, 64), (3, 128), (37, 640), (300, 5120)])
+# row lengths on each register-resident path (up to 2, 4, 8 and 16 chunks of 8 values per lane) and
+# past it (8,256 values: the two-pass kernel)
+@pytest.mark.parametrize("m,k", [(1, 64), (3, 128), (37, 640), (5, 1536), (4, 4096), (300, 5120), (3, 8192),
+                                 (3, 8256)])
 def test_quantize_rows_bit_exact(m, k):
     x = wan_inputs.random_activations(m, k, seed=100 + m, device="cuda")
     x[0, :] = 0.0                                    # a zero row: scale 1, codes 0

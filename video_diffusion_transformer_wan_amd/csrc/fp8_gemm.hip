@@ -7,7 +7,8 @@
 // saturating round to nearest even) is the one of this library's 8-bit attention.
 //
 // Kernels:
-//  * fp8_quant_rows_kernel -- one wave per row: amax, then codes = e4m3fn(clamp(x * 448/amax)).
+//  * fp8_quant_rows_kernel -- one wave per row: amax, then codes = e4m3fn(clamp(x * 448/amax));
+//    rows of up to 8,192 values are held in registers between the two (fp8_quant_rows_reg_kernel).
 //  * fp8_amax_kernel, fp8_quant_tensor_kernel, fp8_finish_scale_kernel -- the per-tensor path:
 //    the tensor's amax by an atomic max on the float bits (order-independent), the codes, and the
 //    scale, all through the caller's scale word.
@@ -100,6 +101,42 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* x, 
   u32x2_t* dst = reinterpret_cast<u32x2_t*>(codes + row * cols);
   for (int c = lane; c < chunks; c += 64) dst[c] = quant8(src[c], inv);
 }
+
+// The same for rows of at most 64 * kPer * 8 values: the row is read from HBM once into registers
+// (kPer 16-byte chunks per lane, loads issued together), then its amax and its codes.
+template <int kPer>
+__global__ __launch_bounds__(256) void fp8_quant_rows_reg_kernel(const uint16_t* x, int64_t rows, int cols,
+                                                                 uint8_t* codes, float* scales) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;   // whole waves leave together
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + row * cols);
+  const int chunks = cols / 8;
+  u32x4_t v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k;
+    v[k] = c < chunks ? src[c] : u32x4_t{0u, 0u, 0u, 0u};
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    float f[8];
+    unpack8(v[k], f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  }
+  amax = wave_max(amax);
+  const float inv = amax > 0.0f ? __fdiv_rn(kE4m3Max, amax) : 1.0f;
+  if (lane == 0) scales[row] = amax > 0.0f ? __fdiv_rn(amax, kE4m3Max) : 1.0f;
+  u32x2_t* dst = reinterpret_cast<u32x2_t*>(codes + row * cols);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int c = lane + 64 * k;
+    if (c < chunks) dst[c] = quant8(v[k], inv);
+  }
+}
+constexpr int kQuantRegChunks = 16;   // rows of up to 8,192 values take the register path
 
 // ---------------------------------------------------------------------------------------------
 // Per-tensor quantisation.  The caller's scale word first collects the bits of the tensor's amax
@@ -368,8 +405,21 @@ __global__ __launch_bounds__(kGThreads, 1) void fp8_gemm_kernel(const GemmParams
 
 hipError_t launch_fp8_quantize_rows(const void* x, int64_t rows, int64_t cols, void* codes, float* scales,
                                     hipStream_t stream) {
-  hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), rows, (int)cols, static_cast<uint8_t*>(codes), scales);
+  const dim3 grid((unsigned)ceil_div(rows, 4));
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  uint8_t* cs = static_cast<uint8_t*>(codes);
+  const int64_t per = ceil_div(cols / 8, 64);   // 16-byte chunks per lane
+  if (per <= 2)
+    hipLaunchKernelGGL(fp8_quant_rows_reg_kernel<2>, grid, dim3(256), 0, stream, xs, rows, (int)cols, cs, scales);
+  else if (per <= 4)
+    hipLaunchKernelGGL(fp8_quant_rows_reg_kernel<4>, grid, dim3(256), 0, stream, xs, rows, (int)cols, cs, scales);
+  else if (per <= 8)
+    hipLaunchKernelGGL(fp8_quant_rows_reg_kernel<8>, grid, dim3(256), 0, stream, xs, rows, (int)cols, cs, scales);
+  else if (per <= kQuantRegChunks)
+    hipLaunchKernelGGL(fp8_quant_rows_reg_kernel<kQuantRegChunks>, grid, dim3(256), 0, stream, xs, rows, (int)cols,
+                       cs, scales);
+  else
+    hipLaunchKernelGGL(fp8_quant_rows_kernel, grid, dim3(256), 0, stream, xs, rows, (int)cols, cs, scales);
   return hipGetLastError();
 }
 
