@@ -82,13 +82,31 @@ __device__ __forceinline__ float smooth_factor(float aq, float ak) {
   return (aq > 0.0f && ak > 0.0f) ? sqrtf(__fdiv_rn(ak, aq)) : 1.0f;
 }
 
+// Per (batch, head, channel), once: the smoothing factor and the V scale from the channel maxima,
+// then the three per-channel multipliers the quantisation kernels apply, written over the maxima:
+// chan_max[bh][0][c] <- smooth (Q), [1][c] <- 1/smooth (K), [2][c] <- 448/max|V| (V; 1 if 0).
+__global__ __launch_bounds__(kThreads) void chan_factor_kernel(float* chan_max, float* smooth, float* v_scale,
+                                                               int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;   // bh * 128 + c
+  if (i >= n) return;
+  const int bh = i / kHeadDim, c = i - bh * kHeadDim;
+  float* cm = chan_max + (int64_t)bh * 3 * kHeadDim + c;
+  const float aq = cm[0], ak = cm[kHeadDim], av = cm[2 * kHeadDim];
+  const float a = smooth_factor(aq, ak);
+  smooth[i] = a;
+  v_scale[i] = av > 0.0f ? __fdiv_rn(av, 448.0f) : 1.0f;
+  cm[0] = a;
+  cm[kHeadDim] = __fdiv_rn(1.0f, a);
+  cm[2 * kHeadDim] = av > 0.0f ? __fdiv_rn(448.0f, av) : 1.0f;
+}
+
 // One 64-token block of Q (blockIdx.z = 0) or K (1): scale by smooth (Q) or 1/smooth (K), block
-// absmax, int8 codes, scale.
+// absmax, int8 codes, scale.  chan_max holds the multipliers of chan_factor_kernel.
 __global__ __launch_bounds__(kThreads) void quant_qk_kernel(const uint16_t* q, const uint16_t* k,
                                                             int heads, int s_q, int s_kv,
                                                             const float* chan_max, int8_t* q_codes,
                                                             float* q_scale, int8_t* k_codes,
-                                                            float* k_scale, float* smooth) {
+                                                            float* k_scale) {
   const int tensor = blockIdx.z;
   const int bh = blockIdx.y;
   const int blk = blockIdx.x;
@@ -103,15 +121,9 @@ __global__ __launch_bounds__(kThreads) void quant_qk_kernel(const uint16_t* q, c
   const int64_t head_off = ((int64_t)b * s * heads + h) * kHeadDim + 8 * cs;
 
   float factor[8];
-  const float* cmq = chan_max + (int64_t)bh * 3 * kHeadDim;
-  const float* cmk = cmq + kHeadDim;
+  const float* fac = chan_max + ((int64_t)bh * 3 + tensor) * kHeadDim + 8 * cs;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = 8 * cs + i;
-    const float a = smooth_factor(cmq[c], cmk[c]);
-    factor[i] = tensor == 0 ? a : __fdiv_rn(1.0f, a);
-    if (tensor == 0 && blk == 0 && row == 0) smooth[(int64_t)bh * kHeadDim + c] = a;
-  }
+  for (int i = 0; i < 8; ++i) factor[i] = fac[i];
 
   float x[4][8];
   float amax = 0.0f;
@@ -163,10 +175,12 @@ __device__ __forceinline__ unsigned cvt_fp8x2(float a, float b) {
 }
 
 // One 64-token block of V: e4m3 codes with the per-channel scale, written transposed to
-// v_codes[bh][c][s_kv_pad]; tokens past s_kv get code 0.
+// v_codes[bh][c][s_kv_pad]; tokens past s_kv get code 0.  chan_max holds the multipliers of
+// chan_factor_kernel.  The transposing LDS tile has rows of 68 bytes: with 64 the 16 lanes that
+// write one channel byte each (channels 8 apart) all hit one bank.
+constexpr int kVRow = kQuantBlock + 4;
 __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* v, int heads, int s_kv,
-                                                           const float* chan_max, uint8_t* v_codes,
-                                                           float* v_scale) {
+                                                           const float* chan_max, uint8_t* v_codes) {
   const int bh = blockIdx.y;
   const int blk = blockIdx.x;
   const int b = bh / heads, h = bh - (bh / heads) * heads;
@@ -179,13 +193,9 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* v, in
 
   float inv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float a = cmv[8 * cs + i];
-    inv[i] = a > 0.0f ? __fdiv_rn(448.0f, a) : 1.0f;
-    if (blk == 0 && row == 0) v_scale[(int64_t)bh * kHeadDim + 8 * cs + i] = a > 0.0f ? __fdiv_rn(a, 448.0f) : 1.0f;
-  }
+  for (int i = 0; i < 8; ++i) inv[i] = cmv[8 * cs + i];
 
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][kQuantBlock];   // [channel][token]
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kHeadDim][kVRow];   // [channel][token]
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int tl = it * 16 + row;
@@ -204,13 +214,13 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(const uint16_t* v, in
     }
   }
   __syncthreads();
-  // 128 channels x 64 bytes; thread writes 32 bytes of one channel
+  // 128 channels x 64 bytes; thread writes 32 bytes of one channel (rows are 4-byte aligned)
   const int c = threadIdx.x >> 1, half = threadIdx.x & 1;
-  const u32x4_t* srcrow = reinterpret_cast<const u32x4_t*>(&tile[c][32 * half]);
+  const unsigned* srcrow = reinterpret_cast<const unsigned*>(&tile[c][32 * half]);
   u32x4_t* dst = reinterpret_cast<u32x4_t*>(v_codes + ((int64_t)bh * kHeadDim + c) * s_pad +
                                             (int64_t)blk * kQuantBlock + 32 * half);
-  dst[0] = srcrow[0];
-  dst[1] = srcrow[1];
+  dst[0] = u32x4_t{srcrow[0], srcrow[1], srcrow[2], srcrow[3]};
+  dst[1] = u32x4_t{srcrow[4], srcrow[5], srcrow[6], srcrow[7]};
 }
 
 }  // namespace
@@ -226,13 +236,16 @@ hipError_t launch_attn8_quantize(const void* q, const void* k, const void* v, co
   hipLaunchKernelGGL(chan_max_kernel, dim3((unsigned)ceil_div(smax, kChanChunk), bh, 3), dim3(kThreads),
                      0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), (int)sh.heads, (int)sh.s_q, (int)sh.s_kv, chan_max);
+  const int n_ch = bh * kHeadDim;
+  hipLaunchKernelGGL(chan_factor_kernel, dim3((n_ch + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
+                     chan_max, smooth, v_scale, n_ch);
   hipLaunchKernelGGL(quant_qk_kernel, dim3((unsigned)ceil_div(smax, kQuantBlock), bh, 2), dim3(kThreads),
                      0, stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      (int)sh.heads, (int)sh.s_q, (int)sh.s_kv, chan_max, q_codes, q_scale, k_codes,
-                     k_scale, smooth);
+                     k_scale);
   hipLaunchKernelGGL(quant_v_kernel, dim3((unsigned)ceil_div(sh.s_kv, kQuantBlock), bh), dim3(kThreads),
                      0, stream, static_cast<const uint16_t*>(v), (int)sh.heads, (int)sh.s_kv, chan_max,
-                     v_codes, v_scale);
+                     v_codes);
   return hipGetLastError();
 }
 
