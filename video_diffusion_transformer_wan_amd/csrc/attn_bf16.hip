@@ -138,6 +138,11 @@ __device__ __forceinline__ u32x4_t rsrc_words32(const void* base, unsigned bytes
 __device__ __forceinline__ void dma_b128(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
   asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
 }
+// The same with the non-temporal hint, for data read once (the next work item's Q): it streams
+// past the caches instead of displacing the K/V tiles that the CUs of an XCD share in L2.
+__device__ __forceinline__ void dma_b128_nt(u32x4_t rsrc, unsigned lds_addr, unsigned voff) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_addr));
+}
 
 // [stage][K | V]: K rows permuted by swap23 and XOR-swizzled by (row % 16); V rows (keys) in
 // natural order, 16-byte chunks XOR-swizzled by 4 * (key % 4).
@@ -520,7 +525,7 @@ __device__ __forceinline__ int attn_tile(kernarg_params_t* kp, const int item, c
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int r = 32 * wv + 4 * i + sub;   // row of the tile; its row in the stage is r % 128
-          dma_b128(qr, dst + 1024 * i, (unsigned)r * stride32 + 16 * (pos ^ (r & 15)));
+          dma_b128_nt(qr, dst + 1024 * i, (unsigned)r * stride32 + 16 * (pos ^ (r & 15)));
         }
         prefetched = true;
       }
@@ -573,7 +578,8 @@ __device__ __forceinline__ int attn_tile(kernarg_params_t* kp, const int item, c
           const int r = 4 * i + sub;   // row of the wave's 32
           const u32x4_t x = *reinterpret_cast<const u32x4_t*>(ost + r * 256 + 16 * pos);
           if (row0 + 4 * i < pe.s_q)
-            *reinterpret_cast<u32x4_t*>(obase_row + i * row_step + 8 * (pos ^ (r & 15))) = x;
+            // non-temporal: O is written once and not read back here
+            __builtin_nontemporal_store(x, reinterpret_cast<u32x4_t*>(obase_row + i * row_step + 8 * (pos ^ (r & 15))));
         }
       }
       if constexpr (kExact) {
