@@ -33,6 +33,9 @@
 //    160 cycles each, against 6 on an idle pipe).
 //  * Workgroups are numbered so that the 32 CUs of one XCD work on consecutive query tiles of the
 //    same head and share its K/V stream in their L2.
+//  * At a work-item boundary the O rows leave through LDS as whole rows and the next item's Q
+//    arrives through LDS, both with the non-temporal hint (read or written once); for short key
+//    sequences half the workgroups start late, so that the CUs do not all cross a boundary at once.
 
 #include <type_traits>
 
