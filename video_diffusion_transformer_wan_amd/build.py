@@ -17,8 +17,8 @@ CEILING_LIB = os.path.join(PKG, "libwan_mfma_ceiling.so")
 ARCH = "gfx950"
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in the device code.  -fno-honor-nans: the kernels
 # never see NaNs (inputs are finite, masks use -1e30), which lets max chains use v_max3_f32.
-# -amdgpu-mfma-vgpr-form: MFMA builtins accumulate in VGPRs even in a kernel that also uses AGPRs
-# (the backward pins its gradient accumulators there); kernels without AGPRs compile the same.
+# -amdgpu-mfma-vgpr-form: MFMA builtins accumulate in VGPRs even in a kernel that also pins other
+# accumulators to AGPRs by inline asm; kernels without AGPRs compile the same.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-shared", f"--offload-arch={ARCH}", "-fno-honor-nans",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-command-line-argument"]

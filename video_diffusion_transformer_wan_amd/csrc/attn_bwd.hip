@@ -7,9 +7,10 @@
 // (the chain rule through the row softmax; D_i = sum_j P_ij dP_ij = dO_i . O_i).
 //
 // Kernels:
-//  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) and D = rowsum(dO * O) per query row, f32, per
-//    64-row query tile [b*H][s_q_pad / 64][lse2 x 64 | D x 64]; padding rows get lse2 = 1e30 (so
-//    P = 0) and D = 0.
+//  * attn_bwd_prep_kernel -- lse2 = lse * log2(e) - 15 and D * 2^-15 (D = rowsum(dO * O)) per
+//    query row, f32, per 64-row query tile [b*H][s_q_pad / 64][lse2 x 64 | D x 64]; padding rows
+//    get lse2 = 1e30 (so P = 0) and D = 0.  With these, exp2(S log2(e) / sqrt(128) - lse2) is
+//    P * 2^15: the dQ kernel scales dQ back at the end, the dK/dV kernel dV and (through D) dS.
 //  * attn_bwd_dq_kernel -- one workgroup = 8 waves = 256 query rows of one (batch, head); each lane
 //    owns one query row (transposed products, as in the forward):
 //        S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
@@ -21,8 +22,8 @@
 //        P wave:  S = Q K^T, P,             dV^T += dO^T P
 //        dS wave: dP = dO V^T, dS = P (dP - D), dK^T += Q^T dS   (P from the P wave through LDS)
 //    (A = Q, dO rows and, by transposing LDS reads, dO^T, Q^T; B = K^T or V^T in VGPRs, P or dS
-//    from VGPRs), looping over 64-query tiles of Q, dO and the row statistics (4-stage LDS ring)
-//    in 32-query blocks; the two waves of a pair alternate between MFMA and VALU phases.
+//    from VGPRs), looping over 64-query tiles of Q, dO and the row statistics (4-stage LDS ring);
+//    the two waves of a pair alternate between MFMA and VALU phases, one tile per phase.
 // Rows read as MFMA A operands go through a read-time permutation (bits 2 and 3 of the row index
 // swapped inside each 32-row block) so that the 8 values a lane feeds a later MFMA from its
 // accumulators belong to 8 consecutive rows; the transposing reads (ds_read_b64_tr_b16) hand
@@ -31,6 +32,8 @@
 // reads and the transposing reads.
 
 #include "wan_attn_internal.h"
+
+#include <type_traits>
 
 namespace wan {
 namespace {
@@ -54,6 +57,12 @@ constexpr float kInvSqrtD = 0.08838834764831845f;    // 1 / sqrt(128)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kPadLse2 = 1.0e30f;            // exp2(s * kScaleLog2 - kPadLse2) == 0
 constexpr float kNeg = -1.0e30f;
+// The row statistics carry P scaled by 2^15: lse2 is stored minus 15 and D times 2^-15, so that
+// exp2(s * kScaleLog2 - lse2) gives P * 2^15 (at most 32768, and at least 2^-14, the smallest
+// normal half, wherever P >= 2^-29), which the dK/dV kernel passes between waves as a half.
+constexpr float kPScaleLog2 = 15.0f;
+constexpr float kPScale = 32768.0f;
+constexpr float kPUnscale = 1.0f / 32768.0f;
 constexpr unsigned kRsrcFlags = 0x00020000u;   // raw buffer, 32-bit dwords
 
 struct BwdParams {
@@ -63,7 +72,7 @@ struct BwdParams {
   const uint16_t* o;
   const uint16_t* d_o;
   const float* lse;   // [b*H][s_q]
-  float* stats;       // per 64-row query tile: lse2 of its rows, then D: [b*H][s_q_pad / 64][2][64]
+  float* stats;       // per 64-row query tile: lse2 - 15 of its rows, then D * 2^-15: [b*H][s_q_pad / 64][2][64]
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -86,6 +95,24 @@ __device__ __forceinline__ unsigned cvt_pk_bf16(float lo, float hi) {
   r[0] = (__bf16)lo;
   r[1] = (__bf16)hi;
   return __builtin_bit_cast(unsigned, r);
+}
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+__device__ __forceinline__ unsigned cvt_pk_f16(float lo, float hi) {
+  f16x2_t r;
+  r[0] = (_Float16)lo;
+  r[1] = (_Float16)hi;
+  return __builtin_bit_cast(unsigned, r);
+}
+// half (low or high 16 bits of x) times f32 t, one rounding (v_fma_mix_f32 with a zero addend)
+__device__ __forceinline__ float mul_h_lo(unsigned x, float t) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(x), "v"(t));
+  return r;
+}
+__device__ __forceinline__ float mul_h_hi(unsigned x, float t) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(x), "v"(t));
+  return r;
 }
 __device__ __forceinline__ float bf16_lo(unsigned x) { return __builtin_bit_cast(float, x << 16); }
 __device__ __forceinline__ float bf16_hi(unsigned x) { return __builtin_bit_cast(float, x & 0xffff0000u); }
@@ -148,44 +175,14 @@ __device__ __forceinline__ bf16x8_t read_cols(const unsigned char* tile, int t, 
   return __builtin_bit_cast(bf16x8_t, part);
 }
 
-// Gradient accumulation on the matrix cores with the accumulators pinned to AGPRs: acc[i] +=
-// a[i] * b (32x32x16 bf16 MFMAs), one asm block per step.  The accumulators live across the whole
-// key or query sweep and only MFMAs touch them; written as builtins, the compiler would keep them
-// in the same AGPRs as the S and dP products and copy them out and back every tile.  s_nop 2
-// first: the B operand (and, at the first step, the zeroed accumulators) was just written by the
-// VALU, and an MFMA may read a VGPR only 2 wait states after a VALU write to it.  After the sweep,
-// settle_mfma() waits out the last accumulation before the VALU reads the accumulators.  The MFMA
-// blocks are not volatile, so the compiler may interleave them with independent VALU work (a
-// volatile asm statement would end its scheduling region).
-__device__ __forceinline__ void mfma4_acc(f32x16_t (&acc)[4], const bf16x8_t (&a)[4], bf16x8_t b) {
-  asm(
-      "s_nop 2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %0, %4, %8, %0\n\t"
-      "v_mfma_f32_32x32x16_bf16 %1, %5, %8, %1\n\t"
-      "v_mfma_f32_32x32x16_bf16 %2, %6, %8, %2\n\t"
-      "v_mfma_f32_32x32x16_bf16 %3, %7, %8, %3"
-      : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3])
-      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(b));
-}
-__device__ __forceinline__ void settle_mfma(f32x16_t (&acc)[4]) {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15" : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
-}
-
-// Wait for this wave's direct-to-LDS loads (the compiler does not track the inline-asm loads, so
-// the wait is explicit: s_waitcnt vmcnt(0), other counters untouched), then the workgroup barrier:
-// after it every wave's loads have landed and every wave is done with the tile it read before.
-__device__ __forceinline__ void barrier_all() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __syncthreads();
-}
-// Workgroup barrier without any wait (bare s_barrier): the dK/dV kernel waits for its
-// direct-to-LDS loads (s_waitcnt vmcnt) and its LDS writes (kWaitLgkm0) explicitly, where needed.
+// Workgroup barrier without any wait (bare s_barrier): the kernels wait for their direct-to-LDS
+// loads (s_waitcnt vmcnt) and their LDS writes (kWaitLgkm0) explicitly, where needed.
 // The memory clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 constexpr short kWaitLgkm0 = (short)0xC07F;   // s_waitcnt lgkmcnt(0), other counters untouched
 
 // ---------------------------------------------------------------------------------------------
-// Stage 1: lse2 and D (dsum) per query row; 8 lanes per row (16 channels each), rows in
+// Stage 1: lse2 - 15 and D * 2^-15 per query row; 8 lanes per row (16 channels each), rows in
 // [b*H][s_q_pad] order, written to the per-tile layout of BwdParams::stats.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, int64_t total) {
   const int64_t r = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
@@ -211,8 +208,8 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, i
   acc += __shfl_xor(acc, 4);
   if (sub == 0) {
     const int64_t x = stat_index(bh, p.s_q_pad, i);
-    p.stats[x] = i < p.s_q ? p.lse[bh * p.s_q + i] * kLog2e : kPadLse2;
-    p.stats[x + 64] = acc;
+    p.stats[x] = i < p.s_q ? p.lse[bh * p.s_q + i] * kLog2e - kPScaleLog2 : kPadLse2;
+    p.stats[x + 64] = acc * kPUnscale;
   }
 }
 
@@ -267,7 +264,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
     gf[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(gr, off, 0, 0));
   }
   const float lse2 = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow)] : kPadLse2;
-  const float dsum = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow) + 64] : 0.0f;
+  const float dsum = qrow < p.s_q ? p.stats[stat_index(bh, p.s_q_pad, qrow) + 64] * kPScale : 0.0f;
   // waited for here, before any direct-to-LDS load is issued: the compiler does not see those, and
   // would otherwise place its wait for these registers inside the tile loop
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -359,15 +356,17 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
   }
   if (first_group) barrier();
 
-  // dQ = dQ^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of row qrow
+  // dQ = dQ^T * 2^-15 / sqrt(128) (dS carried the factor 2^15 of P); lane owns channels
+  // 32 db + 8 g + 4 h .. +3 of row qrow
   if (qrow < p.s_q) {
     uint16_t* dst = p.dq + (((int64_t)bb * p.s_q + qrow) * p.heads + hh) * kHeadDim + 4 * h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x2_t x = {cvt_pk_bf16(acc[db][4 * g] * kInvSqrtD, acc[db][4 * g + 1] * kInvSqrtD),
-                           cvt_pk_bf16(acc[db][4 * g + 2] * kInvSqrtD, acc[db][4 * g + 3] * kInvSqrtD)};
+        constexpr float sc = kInvSqrtD * kPUnscale;
+        const u32x2_t x = {cvt_pk_bf16(acc[db][4 * g] * sc, acc[db][4 * g + 1] * sc),
+                           cvt_pk_bf16(acc[db][4 * g + 2] * sc, acc[db][4 * g + 3] * sc)};
         *reinterpret_cast<u32x2_t*>(dst + 32 * db + 8 * g) = x;
       }
   }
@@ -377,25 +376,31 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
 // Stage 2b: dK and dV.  One workgroup = 8 waves = 128 keys of one (batch, head).  Waves w and
 // w + 4 (w < 4) own keys 32 w .. 32 w + 31, one key per lane, and share a SIMD.  Wave w (the P
 // wave) computes S = Q K^T, P and dV^T += dO^T P; wave w + 4 (the dS wave) computes dP = dO V^T,
-// dS = P (dP - D) and dK^T += Q^T dS, taking the fp32 P of each block from the P wave through
-// LDS.  Each wave holds one B operand (K^T or V^T) and one accumulator set, so two waves fit on a
-// SIMD, and the pair runs in opposite phases between workgroup barriers: while one wave issues
-// the MFMAs of a 32-query block, the other runs the VALU work of a block (P, or dS).  Per
-// 64-query tile i (blocks 2i and 2i+1), phases 4i .. 4i+3:
-//   4i    P wave: dV += block 2i-1, S of block 2i         dS wave: dS of block 2i-1
-//   4i+1  P wave: P of block 2i (to LDS)                 dS wave: dK += block 2i-1, dP of block 2i
-//   4i+2  P wave: dV += block 2i, S of block 2i+1        dS wave: dS of block 2i
-//   4i+3  P wave: P of block 2i+1 (to LDS)               dS wave: dK += block 2i, dP of block 2i+1
-// then two more phases for block 2n-1.  Q, dO and the row statistics of 64-query tiles stream
-// through a 4-stage LDS ring: tile u is loaded at the start of phase 4u - 10, into the stage of
-// tile u - 4 (last read in phase 4u - 11), and waited for at the end of phase 4u - 1.
+// dS = P (dP - D) and dK^T += Q^T dS, taking P of each 64-query tile from the P wave through
+// LDS.  The pair runs in opposite phases between workgroup barriers, one 64-query tile per phase:
+// while one wave issues the 32 MFMAs of a tile (16 accumulating the previous tile, 16 for the
+// new tile's product), the other runs the VALU work of a tile (P, or dS).  Per tile i:
+//   2i    P wave: dV += tile i-1, S of tile i         dS wave: dS of tile i-1
+//   2i+1  P wave: P of tile i (to LDS)                 dS wave: dK += tile i-1, dP of tile i
+// then two more phases for tile n-1.  Q, dO and the row statistics of 64-query tiles stream
+// through a 4-stage LDS ring: tile t is last read in phase 2t+3 (dK += t), tile u is loaded at the
+// start of phase 2u-4, into the stage of tile u-4, and waited for at the end of phase 2u-1.
+// P crosses from the P wave to the dS wave as a half: the row statistics carry the factor 2^15
+// (kPScaleLog2), so the P wave computes P * 2^15, which a half holds to 11 bits wherever
+// P >= 2^-29 (a bf16 copy of it, scaled back at the end, feeds dV).  Each wave holds one B operand
+// (K^T or V^T), one accumulator set, the S or dP of a tile and the bf16 P or dS of the previous
+// one: 227 VGPRs, so two waves fit on a SIMD.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvStage = 2 * kTileBytes + kStatBytes;   // [Q | dO | statistics], 33 KB
 constexpr int kKvRing = 4;
-constexpr int kPBuf = kKvRing * kKvStage;               // P of one 32-query block per wave pair, 4 KB each
-constexpr int kKvLds = kPBuf + 4 * 4096;                // 148 KB
+constexpr int kPSlot = 4096;                            // half P * 2^15 of one tile per wave pair
+constexpr int kPBuf = kKvRing * kKvStage;
+constexpr int kKvLds = kPBuf + 4 * kPSlot;              // 148 KB
 constexpr int kLoadsPerTile = 5;                        // direct-to-LDS loads per wave per tile
+static_assert(kKvLds <= 160 * 1024, "LDS of one workgroup");
+
+template <bool B> using bconst = std::integral_constant<bool, B>;
 
 __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kKvLds];
@@ -414,8 +419,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
   const int krow = k0 + l32;
   const unsigned lds = (unsigned)(uintptr_t)(lds_void_t*)smem;
 
-  // B operand of this wave's product: K^T (P wave) or V^T (dS wave); lane holds key krow,
-  // channels 16c + 8h .. +7 (keys past s_kv read as zeros and are never stored)
   const int64_t koff = ((int64_t)bb * p.s_kv * p.heads + hh) * kHeadDim * 2 + k0 * stride;
   const int64_t kbytes = (int64_t)(p.s_kv - 1 - k0) * stride + kHeadDim * 2;
   const __amdgpu_buffer_rsrc_t br =
@@ -425,8 +428,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
   for (int c = 0; c < 8; ++c)
     bf[c] = __builtin_bit_cast(
         bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(br, (unsigned)(l32 * stride + 32 * c + 16 * h), 0, 0));
-  // waited for here, before any direct-to-LDS load is issued: the compiler does not see those, and
-  // would otherwise place its wait for these registers inside the tile loop
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int64_t qoff = ((int64_t)bb * p.s_q * p.heads + hh) * kHeadDim * 2;
@@ -436,9 +437,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
   const float* stats = p.stats + stat_index(bh, p.s_q_pad, 0);
   const int n_qt = p.s_q_pad / kTile;
   auto stage = [&](int i) __attribute__((always_inline)) { return smem + (i % kKvRing) * kKvStage; };
-  // tile i: Q and dO rows (2 + 2 blocks of 1 KB per wave) and the 512 bytes of statistics, which
-  // every wave loads (lanes 32-63 repeating lanes 0-31, the same bytes to the same place) so that
-  // all waves issue the same number of loads per tile
   auto issue = [&](int i) __attribute__((always_inline)) {
     const int64_t off = (int64_t)i * kTile * stride;
     const unsigned st = lds + (unsigned)((i % kKvRing) * kKvStage);
@@ -447,16 +445,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
     dma_b128(rsrc_words(stats + (int64_t)i * 2 * kTile, 2 * kTile * 4), st + 2 * kTileBytes,
              (unsigned)(16 * (lane & 31)));
   };
-  // wait until the tile issued before the last `after` tiles has landed (s_waitcnt vmcnt, other
-  // counters untouched)
-  auto wait_tile = [&](int after) __attribute__((always_inline)) {
-    if (after >= 2) __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoadsPerTile));
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);
+  // start of phase 2i: tile i+2 into the stage of tile i-2, last read in phase 2i-1
+  auto issue_at = [&](int i) __attribute__((always_inline)) {
+    if (i + 2 < n_qt) issue(i + 2);
+  };
+  // end of phase 2i+1: tile i+1 has landed (s_waitcnt vmcnt, other counters untouched; tile i+2
+  // may still be in flight)
+  auto wait_next = [&](int i) __attribute__((always_inline)) {
+    if (i + 2 < n_qt) __builtin_amdgcn_s_waitcnt(0x0F70 | kLoadsPerTile);
     else __builtin_amdgcn_s_waitcnt(0x0F70);
   };
 
-  // per-lane byte offsets of the operand reads within a tile, computed once (the empty asm keeps
-  // them in registers instead of being rebuilt from the lane index at every read)
   int rowoff[8], coloff[8];
   {
     const int g4 = lane >> 4, kq = (lane >> 2) & 3, q = lane & 3;
@@ -472,7 +471,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
     asm volatile("" : "+v"(coloff[0]), "+v"(coloff[1]), "+v"(coloff[2]), "+v"(coloff[3]), "+v"(coloff[4]),
                  "+v"(coloff[5]), "+v"(coloff[6]), "+v"(coloff[7]));
   }
-  // A operand rows (read_rows) and transposed columns (read_cols) with the offsets above
   auto rows = [&](const unsigned char* t, int qb, int c) __attribute__((always_inline)) {
     return *reinterpret_cast<const bf16x8_t*>((t + rowoff[c]) + 8192 * qb);
   };
@@ -483,11 +481,10 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
       part[e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((t + coloff[2 * db + e]) + 4096 * step));
     return __builtin_bit_cast(bf16x8_t, part);
   };
-  // this wave pair's P slot: chunk j (4 floats) of lane l at float 4 (64 j + l)
-  float* pslot = reinterpret_cast<float*>(smem + kPBuf + 4096 * kw);
+  unsigned char* pslot = smem + kPBuf + kPSlot * kw;
 
-  // Register r of the S, P, dP or dS block holds query 32 qb + 16 (r / 8) + 8 h + r % 8 of its
-  // tile (this lane's key); its statistics sit at rows 32 qb + 16 (i / 2) + 8 h + 4 (i % 2) .. +3.
+  // Register r of block qb of the S, P, dP or dS tile holds query 32 qb + 16 (r / 8) + 8 h + r % 8
+  // (this lane's key); its statistics sit at rows 32 qb + 16 (i / 2) + 8 h + 4 (i % 2) .. +3.
   auto stat4 = [&](const unsigned char* st, int which, int qb, int i) __attribute__((always_inline)) {
     const float* x = reinterpret_cast<const float*>(st + 2 * kTileBytes) + 64 * which;
     return *reinterpret_cast<const f32x4_t*>(x + 32 * qb + 16 * (i >> 1) + 8 * h + 4 * (i & 1));
@@ -498,149 +495,185 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_bwd_dkdv_kernel(const BwdP
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-  f32x16_t prod;            // S (P wave) or dP (dS wave) of the current block
-  unsigned bop[8];          // bf16 P (P wave) or dS (dS wave) of the block awaiting accumulation
+  f32x16_t prod[2];         // S (P wave) or dP (dS wave) of the current tile, two 32-query blocks
+  unsigned bop[16];         // bf16 P (P wave) or dS (dS wave) of the tile awaiting accumulation
   bf16x8_t pre[4];          // A operands of that accumulation's first step, read ahead
-#pragma unroll
-  for (int k = 0; k < 8; ++k) bop[k] = 0u;
+  f32x4_t sv[2][4];         // statistics of the tile in prod (lse2 - 15 or D * 2^-15)
+  // bop is produced in the VALU phase: the empty volatile asm keeps the compiler from sinking its
+  // conversions past the barrier into the MFMA phase that consumes it
+  auto pin_bop = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(bop[0]), "+v"(bop[1]), "+v"(bop[2]), "+v"(bop[3]), "+v"(bop[4]), "+v"(bop[5]),
+                 "+v"(bop[6]), "+v"(bop[7]));
+    asm volatile("" : "+v"(bop[8]), "+v"(bop[9]), "+v"(bop[10]), "+v"(bop[11]), "+v"(bop[12]), "+v"(bop[13]),
+                 "+v"(bop[14]), "+v"(bop[15]));
+  };
 
-  f32x4_t sv[4];            // statistics of the block in prod (lse2 or D), read ahead for the VALU phase
-
-  // MFMA phase: acc += (transposed A tile at at, half aq) x bop over the two 16-query steps of the
-  // block awaiting accumulation (if `accum`), then prod = (rows of the tile at pt, half pq) x bf (if
-  // `product`) and, for the VALU phase after it, statistic `which` of that block from stage st.
-  // All operand reads are issued ahead, in groups that the scheduling barriers keep in this
-  // order: the accumulation steps (whose operands are older) run first, while the product's rows
-  // arrive, so no MFMA waits for a read issued just before it.
-  auto mfma_phase = [&](bool accum, const unsigned char* at, int aq, bool product, const unsigned char* st,
-                        int poff, int which, int pq) __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(3);
+  // MFMA phase: acc += sum over the 4 steps of 16 queries of (transposed A tile at `at`, step s)
+  // x bop step s (if kAcc); prod[qb] = rows of the tile at pt x bf (if kProd) and the statistic
+  // `which` of that tile for the VALU phase after it.  Eight groups of 4 MFMAs, the accumulation
+  // steps alternating with pairs of product steps (one per block, so no MFMA follows the one it
+  // depends on); each group's LDS operands are read while the group before it runs.
+  auto mfma_phase = [&](auto acc_c, auto prod_c, const unsigned char* at, const unsigned char* st, int poff,
+                        int which) __attribute__((always_inline)) {
+    constexpr bool kAcc = decltype(acc_c)::value;
+    constexpr bool kProd = decltype(prod_c)::value;
     const unsigned char* pt = st + poff;
-    bf16x8_t r0[4], r1[4], c1[4];
-    if (accum) {
+    __builtin_amdgcn_s_setprio(3);
+    // group sequence: kAcc && kProd: A0 P0 A1 P1 A2 P2 A3 P3; only kAcc: A0..A3; only kProd: P0..P3
+    constexpr int kGroups = (kAcc ? 4 : 0) + (kProd ? 4 : 0);
+    auto is_acc = [&](int g) __attribute__((always_inline)) { return kAcc && (!kProd || (g & 1) == 0); };
+    auto gidx = [&](int g) __attribute__((always_inline)) { return (kAcc && kProd) ? (g >> 1) : g; };
+    bf16x8_t ring[2][4];
+    auto read_group = [&](int g, bf16x8_t (&f)[4]) __attribute__((always_inline)) {
+      if (is_acc(g)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) c1[db] = cols(at, 2 * aq + 1, db);
-    }
-    if (product) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) r0[c] = rows(pt, pq, c);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (accum) {
-      const u32x4_t x = {bop[0], bop[1], bop[2], bop[3]};
-      mfma4_acc(acc, pre, __builtin_bit_cast(bf16x8_t, x));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (product) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) r1[c] = rows(pt, pq, 4 + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[i] = stat4(st, which, pq, i);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (accum) {
-      const u32x4_t x = {bop[4], bop[5], bop[6], bop[7]};
-      mfma4_acc(acc, c1, __builtin_bit_cast(bf16x8_t, x));
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (product) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f32x16_t zero = {};
-        prod = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r0[c], bf[c], c == 0 ? zero : prod, 0, 0, 0);
+        for (int db = 0; db < 4; ++db) f[db] = cols(at, gidx(g), db);
+      } else {
+        const int c2 = 2 * gidx(g);
+        f[0] = rows(pt, 0, c2);
+        f[1] = rows(pt, 1, c2);
+        f[2] = rows(pt, 0, c2 + 1);
+        f[3] = rows(pt, 1, c2 + 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    const f32x16_t zero = {};
+    if constexpr (!kAcc) read_group(0, ring[0]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) prod = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r1[c], bf[4 + c], prod, 0, 0, 0);
+    for (int g = 0; g < kGroups; ++g) {
+      const int cur = g & 1;
+      if (g + 1 < kGroups) read_group(g + 1, ring[cur ^ 1]);
+      if (kProd && g == kGroups - 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sv[0][i] = stat4(st, which, 0, i);
+      }
+      if (is_acc(g)) {
+        const int s = gidx(g);
+        const u32x4_t x = {bop[4 * s], bop[4 * s + 1], bop[4 * s + 2], bop[4 * s + 3]};
+        const bf16x8_t b = __builtin_bit_cast(bf16x8_t, x);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(g == 0 ? pre[db] : ring[cur][db], b, acc[db], 0, 0, 0);
+      } else {
+        const int c2 = 2 * gidx(g);
+        const bf16x8_t (&f)[4] = ring[cur];
+        prod[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[0], bf[c2], c2 == 0 ? zero : prod[0], 0, 0, 0);
+        prod[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[1], bf[c2], c2 == 0 ? zero : prod[1], 0, 0, 0);
+        prod[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[2], bf[c2 + 1], prod[0], 0, 0, 0);
+        prod[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[3], bf[c2 + 1], prod[1], 0, 0, 0);
+      }
+      if (g + 1 < kGroups) {
+        if (is_acc(g + 1)) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      }
+      if (kProd && g == kGroups - 2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
   issue(0);
   if (n_qt > 1) issue(1);
-  if (n_qt > 2) issue(2);
-  wait_tile(min(n_qt - 1, 2));
+  wait_next(-1);
   barrier();
 
   if (pwave) {
-    // VALU phase: the dO^T operands of this block's first dV step; P of the block (tile at st,
-    // half qb) from prod and its lse2 (sv): fp32 P to the pair's slot, bf16 P to bop
-    auto valu_phase = [&](const unsigned char* st, int qb) __attribute__((always_inline)) {
+    // VALU phase: P * 2^15 of the tile at st from prod and lse2 - 15 (sv): bf16 to bop, half to the
+    // pair's slot; the dO^T operands of the tile's first dV step and the statistics of the tile's
+    // second block are read meanwhile
+    auto valu_phase = [&](const unsigned char* st) __attribute__((always_inline)) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) pre[db] = cols(st + kTileBytes, 2 * qb, db);
+      for (int db = 0; db < 4; ++db) pre[db] = cols(st + kTileBytes, 0, db);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[1][i] = stat4(st, 0, 1, i);
       __builtin_amdgcn_sched_barrier(0);
-      f32x4_t pv[4];
+      u32x2_t hp[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 2 * k;
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(prod[r], kScaleLog2, -sv[r >> 2][r & 3]));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(prod[r + 1], kScaleLog2, -sv[r >> 2][(r & 3) + 1]));
-        bop[k] = cvt_pk_bf16(p0, p1);
-        pv[r >> 2][r & 3] = p0;
-        pv[r >> 2][(r & 3) + 1] = p1;
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 2 * k;
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(prod[qb][r], kScaleLog2, -sv[qb][r >> 2][r & 3]));
+          const float p1 =
+              __builtin_amdgcn_exp2f(__builtin_fmaf(prod[qb][r + 1], kScaleLog2, -sv[qb][r >> 2][(r & 3) + 1]));
+          bop[8 * qb + k] = cvt_pk_bf16(p0, p1);
+          hp[4 * qb + (k >> 1)][k & 1] = cvt_pk_f16(p0, p1);
+        }
+#pragma unroll
+        for (int j = 2 * qb; j < 2 * qb + 2; ++j) {
+          const u32x4_t x = {hp[2 * j][0], hp[2 * j][1], hp[2 * j + 1][0], hp[2 * j + 1][1]};
+          *reinterpret_cast<u32x4_t*>(pslot + 16 * (64 * j + lane)) = x;
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t*>(pslot + 4 * (64 * j + lane)) = pv[j];
+      pin_bop();
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // P is in LDS before the barrier
     };
-    for (int i = 0; i < n_qt; ++i) {
-      const unsigned char* cur = stage(i);
-      const unsigned char* prv = stage(i + 3);   // tile i - 1
-      mfma_phase(i > 0, prv + kTileBytes, 1, true, cur, 0, 0, 0);
+    issue_at(0);
+    mfma_phase(bconst<false>{}, bconst<true>{}, smem, stage(0), 0, 0);
+    barrier();
+    valu_phase(stage(0));
+    wait_next(0);
+    barrier();
+    for (int i = 1; i < n_qt; ++i) {
+      issue_at(i);
+      mfma_phase(bconst<true>{}, bconst<true>{}, stage(i - 1) + kTileBytes, stage(i), 0, 0);
       barrier();
-      valu_phase(cur, 0);
-      barrier();
-      if (i + 3 < n_qt) issue(i + 3);
-      mfma_phase(true, cur + kTileBytes, 0, true, cur, 0, 0, 1);
-      barrier();
-      valu_phase(cur, 1);
-      wait_tile(min(n_qt - 2 - i, 2));
+      valu_phase(stage(i));
+      wait_next(i);
       barrier();
     }
-    mfma_phase(true, stage(n_qt - 1) + kTileBytes, 1, false, smem, 0, 0, 0);
+    mfma_phase(bconst<true>{}, bconst<false>{}, stage(n_qt - 1) + kTileBytes, smem, 0, 0);
     barrier();
     barrier();
   } else {
-    // VALU phase: dS of the block (tile at st, half qb) from prod (dP), the P wave's fp32 P and D
-    // (sv), to bop; the Q^T operands of this block's first dK step are read meanwhile
-    auto valu_phase = [&](const unsigned char* st, int qb) __attribute__((always_inline)) {
-      f32x4_t pv[4];
+    // VALU phase: dS of the tile at st from prod (dP), the P wave's half P * 2^15 and D * 2^-15
+    // (sv), to bop; the Q^T operands of the tile's first dK step and the statistics of its second
+    // block are read meanwhile
+    auto valu_phase = [&](const unsigned char* st) __attribute__((always_inline)) {
+      u32x4_t pw[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const f32x4_t*>(pslot + 4 * (64 * j + lane));
+      for (int j = 0; j < 4; ++j) pw[j] = *reinterpret_cast<const u32x4_t*>(pslot + 16 * (64 * j + lane));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) pre[db] = cols(st, 2 * qb, db);
+      for (int db = 0; db < 4; ++db) pre[db] = cols(st, 0, db);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[1][i] = stat4(st, 1, 1, i);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int r = 2 * k;
-        const float d0 = prod[r] - sv[r >> 2][r & 3], d1 = prod[r + 1] - sv[r >> 2][(r & 3) + 1];
-        bop[k] = cvt_pk_bf16(pv[r >> 2][r & 3] * d0, pv[r >> 2][(r & 3) + 1] * d1);
-      }
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int r = 2 * k;
+          const unsigned pk = pw[2 * qb + (k >> 2)][k & 3];
+          // (dP - D) * 2^-15, exactly the fp32 dP - D scaled, times the half P * 2^15
+          const float d0 = __builtin_fmaf(prod[qb][r], kPUnscale, -sv[qb][r >> 2][r & 3]);
+          const float d1 = __builtin_fmaf(prod[qb][r + 1], kPUnscale, -sv[qb][r >> 2][(r & 3) + 1]);
+          bop[8 * qb + k] = cvt_pk_bf16(mul_h_lo(pk, d0), mul_h_hi(pk, d1));
+        }
+      pin_bop();
     };
-    for (int i = 0; i < n_qt; ++i) {
-      const unsigned char* cur = stage(i);
-      const unsigned char* prv = stage(i + 3);   // tile i - 1
-      if (i > 0) valu_phase(prv, 1);
+    issue_at(0);
+    barrier();
+    mfma_phase(bconst<false>{}, bconst<true>{}, smem, stage(0), kTileBytes, 1);
+    wait_next(0);
+    barrier();
+    for (int i = 1; i < n_qt; ++i) {
+      issue_at(i);
+      valu_phase(stage(i - 1));
       barrier();
-      mfma_phase(i > 0, prv, 1, true, cur, kTileBytes, 1, 0);
-      barrier();
-      if (i + 3 < n_qt) issue(i + 3);
-      valu_phase(cur, 0);
-      barrier();
-      mfma_phase(true, cur, 0, true, cur, kTileBytes, 1, 1);
-      wait_tile(min(n_qt - 2 - i, 2));
+      mfma_phase(bconst<true>{}, bconst<true>{}, stage(i - 1), stage(i), kTileBytes, 1);
+      wait_next(i);
       barrier();
     }
-    valu_phase(stage(n_qt - 1), 1);
+    valu_phase(stage(n_qt - 1));
     barrier();
-    mfma_phase(true, stage(n_qt - 1), 1, false, smem, 0, 1, 0);
+    mfma_phase(bconst<true>{}, bconst<false>{}, stage(n_qt - 1), smem, 0, 1);
     barrier();
   }
 
-  settle_mfma(acc);
   if (krow < p.s_kv) {
     // dV = dV^T; dK = dK^T * 1/sqrt(128); lane owns channels 32 db + 8 g + 4 h .. +3 of key krow
-    const float scale = pwave ? 1.0f : kInvSqrtD;
+    const float scale = pwave ? kPUnscale : kInvSqrtD;
     uint16_t* dst = (pwave ? p.dv : p.dk) + (((int64_t)bb * p.s_kv + krow) * p.heads + hh) * kHeadDim + 4 * h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
