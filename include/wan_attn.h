@@ -138,7 +138,8 @@ int wan_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, void*
  * S = Q K^T/sqrt(128), P = exp(S - lse) (row softmax), D_i = sum_c dO[i,c] O[i,c]:
  *   dV = P^T dO,   dS = P * (dO V^T - D),   dQ = dS K / sqrt(128),   dK = dS^T Q / sqrt(128)
  * per (batch, head), products in bf16 on the MFMA with fp32 accumulation, P and dS rounded to
- * bf16 for the products, outputs rounded to bf16.
+ * bf16 for the products (the dS that feeds dK is formed from P rounded to 11 significant bits),
+ * outputs rounded to bf16.
  * Inputs: q, k, v as for the forward; o [batch, s_q, heads, 128] bf16 and lse [batch, heads, s_q]
  * f32 from wan_attn_fwd_lse on the same q, k, v; d_o with o's layout.
  * Outputs: dq with q's layout, dk and dv with k's layout, bf16, owned by the caller; none may
