@@ -15,7 +15,7 @@
 //    owns one query row (transposed products, as in the forward):
 //        S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
 //        dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
-//    looping over 64-key tiles of K and V streamed through a 4-stage LDS ring, waves 0-3 and 4-7
+//    looping over 64-key tiles of K and V streamed through a 5-stage LDS ring, waves 0-3 and 4-7
 //    in ping-pong (one group's S^T / dP^T products against the other's VALU work and dQ product).
 //  * attn_bwd_dkdv_kernel -- one workgroup = 8 waves = 128 keys; each lane owns one key, and two
 //    waves share each group of 32 keys (and a SIMD):
@@ -219,21 +219,23 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const BwdParams p, i
 //     S^T = K Q^T,  dP^T = V dO^T   (A = K, V rows from LDS; B = Q^T, dO^T in VGPRs)
 //     dQ^T += K^T dS^T               (A = K^T by transposing LDS reads; B = dS^T from VGPRs)
 // Each wave's work on a 64-key tile is split into two half-steps between workgroup barriers:
-// (1) S^T and dP^T of tile j; (2) the loads of tile j+2, dS of tile j and the dQ product.  Waves
+// (1) S^T and dP^T of tile j; (2) the loads of tile j+3, dS of tile j and the dQ product.  Waves
 // 0-3 and 4-7 share the four SIMDs and run one barrier apart, so each SIMD's matrix core takes one
 // wave's S^T / dP^T products while the other wave runs its VALU work and then its dQ product.
 // The dQ^T accumulators are MFMA builtins in VGPRs (256 per lane, no AGPRs): pinned to AGPRs by
 // inline asm they would make the compiler split the register file 128 / 128, and the S^T, dP^T
 // and operand registers would not fit in 128 VGPRs.  64-key tiles of K and V stream through a
-// 4-stage LDS ring: tile t is loaded at the start of half-step (2) of tile t-2 -- after every read
-// of tile t-4, the last being the second group's dQ product of tile t-4, two barriers earlier --
-// and waited for at the end of half-step (1) of tile t-1, before the barrier after which the first
-// group reads it.
+// 5-stage LDS ring (all 160 KB of the CU's LDS): tile t is loaded at the start of half-step (2) of
+// tile t-3 -- after every read of tile t-5, the last being the second group's dQ product of tile
+// t-5, at least two barriers earlier -- and waited for at the end of half-step (1) of tile t-1,
+// before the barrier after which the first group reads it (tile t+1 may still be in flight: the
+// wait is counted).  The stage offsets rotate in scalar registers (computed as j % 5 they cost the
+// loop 8 spilled VGPRs).  A 4-stage ring, loading two tiles ahead, was 0.65% slower per backward.
 constexpr int kDqWaves = 8;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRows = 32 * kDqWaves;      // 256 query rows per workgroup
 constexpr int kDqStage = 2 * kTileBytes;    // [K | V], 32 KB
-constexpr int kDqRing = 4;
+constexpr int kDqRing = 5;
 
 __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kDqRing * kDqStage];
@@ -274,9 +276,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(p.v) + kvoff;
   const int64_t kvbytes = (int64_t)(p.s_kv - 1) * stride + kHeadDim * 2;
   const int n_kt = (p.s_kv + kTile - 1) / kTile;
-  auto issue = [&](int j) __attribute__((always_inline)) {
+  auto issue_at = [&](int j, int stage_off) __attribute__((always_inline)) {
     const int64_t off = (int64_t)j * kTile * stride;
-    const unsigned st = lds + (unsigned)((j % kDqRing) * kDqStage);
+    const unsigned st = lds + (unsigned)stage_off;
     load_tile<kDqWaves>(kbase + off, kvbytes - off, stride, st, wv, lane);
     load_tile<kDqWaves>(vbase + off, kvbytes - off, stride, st + kTileBytes, wv, lane);
   };
@@ -287,13 +289,18 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
 
-  issue(0);
-  if (n_kt > 1) issue(1);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  issue_at(0, 0);
+  if (n_kt > 1) issue_at(1, kDqStage);
+  if (n_kt > 2) issue_at(2, 2 * kDqStage);
+  // tiles 0 and 1 have landed (tile 2 may be in flight: 4 loads per wave per tile)
+  if (n_kt > 2) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+  else __builtin_amdgcn_s_waitcnt(0x0F70);
   barrier();
   if (!first_group) barrier();
+  int cur_off = 0;                  // stage of tile j
+  int next_off = 3 * kDqStage;      // stage of tile j+3
   for (int j = 0; j < n_kt; ++j) {
-    const unsigned char* ks = smem + (j % kDqRing) * kDqStage;
+    const unsigned char* ks = smem + cur_off;
     const unsigned char* vs = ks + kTileBytes;
     // (1) S^T and dP^T of tile j
     __builtin_amdgcn_s_setprio(3);
@@ -321,11 +328,15 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_bwd_dq_kernel(const BwdPar
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
-    // this wave's loads of tile j+1 (issued in half-step (2) of tile j-1) have landed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // this wave's loads of tile j+1 (issued in half-step (2) of tile j-2) have landed; those of tile
+    // j+2 may not have
+    if (j + 2 < n_kt) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x0F70);
     barrier();
-    // (2) the loads of tile j+2; dS of tile j; dQ^T += K^T dS^T over the tile's 4 steps of 16 keys
-    if (j + 2 < n_kt) issue(j + 2);
+    // (2) the loads of tile j+3; dS of tile j; dQ^T += K^T dS^T over the tile's 4 steps of 16 keys
+    if (j + 3 < n_kt) issue_at(j + 3, next_off);
+    cur_off = cur_off == (kDqRing - 1) * kDqStage ? 0 : cur_off + kDqStage;
+    next_off = next_off == (kDqRing - 1) * kDqStage ? 0 : next_off + kDqStage;
     // register r of key block kb holds key 64 j + 32 kb + 16 (r / 8) + 8 h + r % 8 of this lane's row
     unsigned ds[2][8];
     const int kv0 = j * kTile;
